@@ -1,0 +1,131 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) attention library libattn.so.
+ *
+ * The library computes scaled-dot-product attention
+ *     O = softmax(scale * Q K^T) V          (softmax over the key axis)
+ * in the two forms described in "Speed Is All You Need: On-Device
+ * Acceleration of Large Diffusion Models via GPU-Aware Optimizations"
+ * (Chen et al.), news write-up, section on improving attention efficiency:
+ *
+ *  - partially fused softmax: one pass reduces every row of the logit matrix
+ *    A = scale * Q K^T to an (m, l) pair -- an N x 2 tensor -- with the row
+ *    cut into key blocks whose partial pairs are merged inside the same
+ *    launch; a second pass applies the softmax inside the product with V, so
+ *    softmax(A) is never stored (attn_stats + attn_pv);
+ *  - FlashAttention: one tiled launch that reads Q, K, V once and keeps the
+ *    running softmax state on chip; it is exact, so it reaches the same O
+ *    (attn_flash);
+ *  - the same write-up picks between the two per GPU and head dimension; here
+ *    the choice is made by timing both on the device (attn_select, and
+ *    attn_forward with ATTN_AUTO).
+ *
+ * Definitions used throughout (the pages name the two per-row quantities
+ * only as "L and S"; they are read here as the row maximum and the row sum
+ * of exponentials relative to it, in natural-log units, scale included):
+ *     a_ij = scale * sum_c q_ic k_jc
+ *     m_i  = max_j a_ij
+ *     l_i  = sum_j exp(a_ij - m_i)          (so 1 <= l_i <= Nk)
+ *     O_ic = sum_j exp(a_ij - m_i) v_jc / l_i
+ *
+ * Layouts (all dense, row-major, no strides):
+ *     q, out : [B][H][Nq][d]   element type given by `dt`
+ *     k, v   : [B][H][Nk][d]   element type given by `dt`
+ *     ml     : [B][H][Nq][2]   float32, ml[..][0] = m, ml[..][1] = l
+ * All pointers are DEVICE pointers on the current HIP device.  The caller owns
+ * every buffer; the library allocates nothing on these paths, never frees
+ * caller memory and does not synchronise (attn_select and the first
+ * ATTN_AUTO call for a new shape are the exceptions, see below).  Work is
+ * enqueued on `stream` (a hipStream_t passed as void*, NULL = default stream)
+ * and is complete when that stream is; buffers must stay valid until then.
+ *
+ * Supported: d in {40, 80, 160}; dt in {ATTN_F32, ATTN_F16, ATTN_BF16};
+ * any B, H, Nq, Nk >= 1 with B*H*max(Nq,Nk)*d < 2^31 elements per tensor.
+ * F16/BF16 run on the matrix cores with float32 accumulation and float32
+ * softmax state; F32 is a vector-ALU float32 path kept for exactness checks.
+ *
+ * Errors: arguments are validated before anything is launched; on an error
+ * nothing is written.  A launch failure reported by the HIP runtime is
+ * returned as ATTN_ERR_HIP (outputs are then unspecified).
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* null required pointer, dimension < 1, non-finite
+                               scale, tensor larger than 2^31 - 1 elements */
+  ATTN_ERR_UNSUPPORTED = 2, /* d not in {40, 80, 160}, unknown dtype/variant */
+  ATTN_ERR_HIP = 3          /* the HIP runtime reported an error */
+} attn_status;
+
+typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 } attn_dtype;
+
+typedef enum {
+  ATTN_AUTO = 0,          /* pick by measurement, cached per shape */
+  ATTN_PARTIAL_FUSED = 1, /* attn_stats then attn_pv */
+  ATTN_FLASH = 2          /* attn_flash */
+} attn_variant;
+
+/* Partially fused softmax, pass 1: per-row statistics of A = scale * Q K^T.
+ * Writes ml[b][h][i] = (m_i, l_i).  Each row's key range is cut into blocks;
+ * every block is reduced to its own (max, sum of exp) and the partial pairs
+ * are merged with (m,l)+(m',l') = (M, l e^(m-M) + l' e^(m'-M)), M = max(m,m'),
+ * all inside this single launch (write-up, attention section: the block-split
+ * reduction that raises the parallelism of the A -> (L, S) mapping).
+ * A is recomputed from Q and K, never read from or written to memory.
+ * q: [B][H][Nq][d], k: [B][H][Nk][d] (dt); ml: [B][H][Nq][2] float32, written. */
+attn_status attn_stats(const void* q, const void* k, float* ml, int B, int H, int Nq,
+                       int Nk, int d, float scale, attn_dtype dt, void* stream);
+
+/* Partially fused softmax, pass 2: O = softmax(A) V using the statistics from
+ * attn_stats, with the exponentials, the normalisation and the product with V
+ * fused in one launch (write-up, attention section).
+ * ml: [B][H][Nq][2] float32 as written by attn_stats (read only);
+ * out: [B][H][Nq][d] (dt), written. */
+attn_status attn_pv(const void* q, const void* k, const void* v, const float* ml, void* out,
+                    int B, int H, int Nq, int Nk, int d, float scale, attn_dtype dt,
+                    void* stream);
+
+/* FlashAttention forward: one launch, tiled over keys with the online
+ * (running max / running sum) softmax, exact up to rounding (write-up,
+ * attention section).  ml_out may be NULL; if given, the final (m, l) of every
+ * row is written in the same convention as attn_stats. */
+attn_status attn_flash(const void* q, const void* k, const void* v, void* out, float* ml_out,
+                       int B, int H, int Nq, int Nk, int d, float scale, attn_dtype dt,
+                       void* stream);
+
+/* Full forward.  ATTN_PARTIAL_FUSED runs attn_stats then attn_pv (two
+ * launches) and needs `ml` as scratch/output; ATTN_FLASH runs attn_flash and
+ * writes `ml` if it is non-NULL; ATTN_AUTO uses the cached choice for this
+ * shape, and on the first call for a shape times both variants on the
+ * caller's buffers (synchronising `stream` once) before caching the winner
+ * (if `ml` is NULL only FLASH is eligible).  The environment variable
+ * ATTN_VARIANT=pf|flash overrides ATTN_AUTO. */
+attn_status attn_forward(const void* q, const void* k, const void* v, void* out, float* ml,
+                         int B, int H, int Nq, int Nk, int d, float scale, attn_variant var,
+                         attn_dtype dt, void* stream);
+
+/* The variant ATTN_AUTO uses for this shape.  On a cache miss it allocates
+ * temporary device buffers, times both variants on `stream`, frees the
+ * buffers and caches the winner, so it synchronises and may allocate; call it
+ * outside timed or captured regions.  Returns ATTN_AUTO (0) on error. */
+attn_variant attn_select(int B, int H, int Nq, int Nk, int d, attn_dtype dt, void* stream);
+
+/* Before any measurement the choice follows the write-up's own rule: the
+ * fused single pass for head dimension 40, the two-pass form otherwise. */
+attn_variant attn_default_variant(int d);
+
+/* Forget all cached ATTN_AUTO decisions (thread-safe). */
+void attn_select_reset(void);
+
+/* Static text for a status code. */
+const char* attn_status_string(attn_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ATTN_H */
