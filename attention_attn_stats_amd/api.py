@@ -1,0 +1,121 @@
+"""Python entry points with the same names as the C ABI (include/attn.h).
+
+Argument marshalling only: shapes and element types are checked, pointers and
+the current HIP stream are handed to libattn.so, and any non-OK status is
+raised as AttnError.  Nothing here computes attention.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+from ._lib import AttnError
+
+_DT = {torch.float32: _lib.F32, torch.float16: _lib.F16, torch.bfloat16: _lib.BF16}
+_VAR = {"auto": _lib.AUTO, "pf": _lib.PARTIAL_FUSED, "partial_fused": _lib.PARTIAL_FUSED,
+        "flash": _lib.FLASH}
+_VAR_NAME = {_lib.AUTO: "auto", _lib.PARTIAL_FUSED: "pf", _lib.FLASH: "flash"}
+
+
+def _check(status: int, where: str):
+    if status != _lib.OK:
+        raise AttnError(status, where)
+
+
+def _dims(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, H, N, d]")
+    B, H, Nq, d = q.shape
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != d:
+        raise ValueError(f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    if v is not None and v.shape != k.shape:
+        raise ValueError(f"v shape {tuple(v.shape)} must equal k shape {tuple(k.shape)}")
+    for t in (q, k) + ((v,) if v is not None else ()):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError("q, k, v must be contiguous device tensors of one dtype")
+    if q.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    return B, H, Nq, k.shape[2], d
+
+
+def _scale(scale, d):
+    return float(1.0 / math.sqrt(d)) if scale is None else float(scale)
+
+
+def _stream():
+    return ctypes_stream(torch.cuda.current_stream())
+
+
+def ctypes_stream(s: torch.cuda.Stream):
+    return s.cuda_stream
+
+
+def _ml_for(q, ml):
+    B, H, Nq, _ = q.shape
+    if ml is None:
+        return torch.empty((B, H, Nq, 2), device=q.device, dtype=torch.float32)
+    if ml.shape != (B, H, Nq, 2) or ml.dtype != torch.float32 or not ml.is_contiguous() or not ml.is_cuda:
+        raise ValueError("ml must be a contiguous float32 [B, H, Nq, 2] device tensor")
+    return ml
+
+
+def stats(q, k, ml=None, scale=None):
+    """Row statistics (m, l) of A = scale q k^T -> ml [B, H, Nq, 2] float32."""
+    B, H, Nq, Nk, d = _dims(q, k, None)
+    ml = _ml_for(q, ml)
+    _check(_lib.load().attn_stats(q.data_ptr(), k.data_ptr(), ml.data_ptr(), B, H, Nq, Nk, d,
+                                  _scale(scale, d), _DT[q.dtype], _stream()), "attn_stats")
+    return ml
+
+
+def pv(q, k, v, ml, out=None, scale=None):
+    """O = softmax(A) v from statistics produced by stats()."""
+    B, H, Nq, Nk, d = _dims(q, k, v)
+    if ml.shape != (B, H, Nq, 2) or ml.dtype != torch.float32 or not ml.is_contiguous():
+        raise ValueError("ml must be a contiguous float32 [B, H, Nq, 2] device tensor")
+    out = torch.empty_like(q) if out is None else out
+    _check(_lib.load().attn_pv(q.data_ptr(), k.data_ptr(), v.data_ptr(), ml.data_ptr(), out.data_ptr(),
+                               B, H, Nq, Nk, d, _scale(scale, d), _DT[q.dtype], _stream()), "attn_pv")
+    return out
+
+
+def flash(q, k, v, out=None, ml=None, want_ml=False, scale=None):
+    """Single-pass online-softmax attention.  Returns out, or (out, ml) if
+    want_ml or ml is given."""
+    B, H, Nq, Nk, d = _dims(q, k, v)
+    out = torch.empty_like(q) if out is None else out
+    if want_ml or ml is not None:
+        ml = _ml_for(q, ml)
+    _check(_lib.load().attn_flash(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  ml.data_ptr() if ml is not None else None, B, H, Nq, Nk, d,
+                                  _scale(scale, d), _DT[q.dtype], _stream()), "attn_flash")
+    return (out, ml) if ml is not None else out
+
+
+def forward(q, k, v, variant="auto", out=None, ml=None, scale=None):
+    """Attention with the given variant ('auto', 'pf', 'flash'); returns (out, ml)."""
+    B, H, Nq, Nk, d = _dims(q, k, v)
+    out = torch.empty_like(q) if out is None else out
+    ml = _ml_for(q, ml)
+    _check(_lib.load().attn_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), ml.data_ptr(),
+                                    B, H, Nq, Nk, d, _scale(scale, d), _VAR[variant], _DT[q.dtype],
+                                    _stream()), "attn_forward")
+    return out, ml
+
+
+def select(B, H, Nq, Nk, d, dtype=torch.float16) -> str:
+    """The variant 'auto' uses for this shape ('pf' or 'flash'); may time both."""
+    r = _lib.load().attn_select(B, H, Nq, Nk, d, _DT[dtype], _stream())
+    if r == _lib.AUTO:
+        raise AttnError(_lib.ERR_HIP, "attn_select")
+    return _VAR_NAME[r]
+
+
+def select_reset():
+    _lib.load().attn_select_reset()
+
+
+def default_variant(d: int) -> str:
+    return _VAR_NAME[_lib.load().attn_default_variant(int(d))]

@@ -1,0 +1,262 @@
+// C ABI of libattn.so: argument validation, dispatch to the kernels and the
+// per-shape choice between the two attention forms.
+//
+// The choice mirrors "Speed Is All You Need" (Chen et al., news write-up,
+// section on improving attention efficiency), where FlashAttention is used
+// selectively -- for head dimension 40 on the GPUs studied, the partially
+// fused softmax elsewhere -- because its kernel is register hungry.  Here the
+// rule only seeds the default; ATTN_AUTO decides per shape by timing both
+// forms on the device and caching the faster.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
+
+#include "attn.h"
+#include "attn_internal.h"
+
+namespace {
+
+using attn::Problem;
+
+bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
+
+attn_status check_common(int B, int H, int Nq, int Nk, int d, float scale, attn_dtype dt) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_INVALID_ARG;
+  if (dt != ATTN_F32 && dt != ATTN_F16 && dt != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (d != 40 && d != 80 && d != 160) return ATTN_ERR_UNSUPPORTED;
+  const long long bh = (long long)B * H;
+  const long long lim = 0x7fffffffLL;
+  if (bh > lim || bh * Nq > lim / 2 || bh * Nq * d > lim || bh * Nk * d > lim) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+Problem make(const void* q, const void* k, const void* v, void* out, float* ml, int B, int H, int Nq,
+             int Nk, int d, float scale, attn_dtype dt, void* stream) {
+  Problem p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.ml = ml;
+  p.BH = B * H;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.d = d;
+  p.scale = scale;
+  p.dt = dt;
+  p.stream = (hipStream_t)stream;
+  return p;
+}
+
+attn_status to_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+attn_status run_stats(const Problem& p) {
+  return to_status(p.dt == ATTN_F32 ? attn::launch_f32_stats(p) : attn::launch_mfma_stats(p));
+}
+attn_status run_pv(const Problem& p) {
+  return to_status(p.dt == ATTN_F32 ? attn::launch_f32_pv(p) : attn::launch_mfma_pv(p));
+}
+attn_status run_flash(const Problem& p) {
+  return to_status(p.dt == ATTN_F32 ? attn::launch_f32_flash(p) : attn::launch_mfma_flash(p));
+}
+attn_status run_pf(const Problem& p) {
+  attn_status s = run_stats(p);
+  return s == ATTN_OK ? run_pv(p) : s;
+}
+
+// ---- variant cache -------------------------------------------------------
+typedef std::tuple<int, int, int, int, int, int> Key;  // BH, Nq, Nk, d, dtype, device
+std::mutex g_mu;
+std::map<Key, attn_variant> g_cache;
+
+attn_variant env_override() {
+  const char* e = std::getenv("ATTN_VARIANT");
+  if (!e) return ATTN_AUTO;
+  if (!std::strcmp(e, "pf") || !std::strcmp(e, "partial_fused")) return ATTN_PARTIAL_FUSED;
+  if (!std::strcmp(e, "flash")) return ATTN_FLASH;
+  return ATTN_AUTO;
+}
+
+int select_iters() {
+  const char* e = std::getenv("ATTN_SELECT_ITERS");
+  const int n = e ? std::atoi(e) : 5;
+  return std::min(std::max(n, 1), 100);
+}
+
+Key key_of(const Problem& p) {
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  return Key(p.BH, p.Nq, p.Nk, p.d, (int)p.dt, dev);
+}
+
+// Median time (ms) of `iters` runs of one variant, after one warm-up run.
+attn_status time_variant(const Problem& p, attn_variant var, int iters, float* ms_out) {
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess) return ATTN_ERR_HIP;
+  if (hipEventCreate(&e1) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return ATTN_ERR_HIP;
+  }
+  attn_status st = var == ATTN_FLASH ? run_flash(p) : run_pf(p);
+  float times[100];
+  for (int i = 0; i < iters && st == ATTN_OK; ++i) {
+    if (hipEventRecord(e0, p.stream) != hipSuccess) st = ATTN_ERR_HIP;
+    if (st == ATTN_OK) st = var == ATTN_FLASH ? run_flash(p) : run_pf(p);
+    if (st == ATTN_OK && hipEventRecord(e1, p.stream) != hipSuccess) st = ATTN_ERR_HIP;
+    if (st == ATTN_OK && hipEventSynchronize(e1) != hipSuccess) st = ATTN_ERR_HIP;
+    if (st == ATTN_OK && hipEventElapsedTime(&times[i], e0, e1) != hipSuccess) st = ATTN_ERR_HIP;
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (st != ATTN_OK) return st;
+  std::sort(times, times + iters);
+  *ms_out = times[iters / 2];
+  return ATTN_OK;
+}
+
+// Times both variants on the problem's buffers and returns the faster; the
+// last run is the winner's, so the outputs are those of the chosen variant.
+attn_status measure(const Problem& p, attn_variant* out) {
+  const int iters = select_iters();
+  float t_pf = 0.f, t_fl = 0.f;
+  attn_status st = time_variant(p, ATTN_PARTIAL_FUSED, iters, &t_pf);
+  if (st == ATTN_OK) st = time_variant(p, ATTN_FLASH, iters, &t_fl);
+  if (st != ATTN_OK) return st;
+  *out = t_fl <= t_pf ? ATTN_FLASH : ATTN_PARTIAL_FUSED;
+  if (*out == ATTN_PARTIAL_FUSED) st = run_pf(p);  // FLASH already ran last
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension, element type or variant";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+attn_variant attn_default_variant(int d) { return d == 40 ? ATTN_FLASH : ATTN_PARTIAL_FUSED; }
+
+attn_status attn_stats(const void* q, const void* k, float* ml, int B, int H, int Nq, int Nk, int d,
+                       float scale, attn_dtype dt, void* stream) {
+  if (!q || !k || !ml || !aligned16(q) || !aligned16(k) || ((uintptr_t)ml & 7u)) return ATTN_ERR_INVALID_ARG;
+  attn_status s = check_common(B, H, Nq, Nk, d, scale, dt);
+  if (s != ATTN_OK) return s;
+  return run_stats(make(q, k, nullptr, nullptr, ml, B, H, Nq, Nk, d, scale, dt, stream));
+}
+
+attn_status attn_pv(const void* q, const void* k, const void* v, const float* ml, void* out, int B, int H,
+                    int Nq, int Nk, int d, float scale, attn_dtype dt, void* stream) {
+  if (!q || !k || !v || !ml || !out) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || ((uintptr_t)ml & 7u))
+    return ATTN_ERR_INVALID_ARG;
+  attn_status s = check_common(B, H, Nq, Nk, d, scale, dt);
+  if (s != ATTN_OK) return s;
+  return run_pv(make(q, k, v, out, const_cast<float*>(ml), B, H, Nq, Nk, d, scale, dt, stream));
+}
+
+attn_status attn_flash(const void* q, const void* k, const void* v, void* out, float* ml_out, int B, int H,
+                       int Nq, int Nk, int d, float scale, attn_dtype dt, void* stream) {
+  if (!q || !k || !v || !out) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || ((uintptr_t)ml_out & 7u))
+    return ATTN_ERR_INVALID_ARG;
+  attn_status s = check_common(B, H, Nq, Nk, d, scale, dt);
+  if (s != ATTN_OK) return s;
+  return run_flash(make(q, k, v, out, ml_out, B, H, Nq, Nk, d, scale, dt, stream));
+}
+
+attn_status attn_forward(const void* q, const void* k, const void* v, void* out, float* ml, int B, int H,
+                         int Nq, int Nk, int d, float scale, attn_variant var, attn_dtype dt, void* stream) {
+  if (!q || !k || !v || !out) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || ((uintptr_t)ml & 7u))
+    return ATTN_ERR_INVALID_ARG;
+  if (var != ATTN_AUTO && var != ATTN_PARTIAL_FUSED && var != ATTN_FLASH) return ATTN_ERR_UNSUPPORTED;
+  attn_status s = check_common(B, H, Nq, Nk, d, scale, dt);
+  if (s != ATTN_OK) return s;
+  if (var == ATTN_PARTIAL_FUSED && !ml) return ATTN_ERR_INVALID_ARG;
+  const Problem p = make(q, k, v, out, ml, B, H, Nq, Nk, d, scale, dt, stream);
+  if (var == ATTN_AUTO) {
+    const attn_variant forced = env_override();
+    if (forced != ATTN_AUTO) var = forced;
+    if (var == ATTN_PARTIAL_FUSED && !ml) var = ATTN_FLASH;
+  }
+  if (var == ATTN_AUTO) {
+    if (!ml) return run_flash(p);
+    const Key key = key_of(p);
+    {
+      std::lock_guard<std::mutex> g(g_mu);
+      auto it = g_cache.find(key);
+      if (it != g_cache.end()) var = it->second;
+    }
+    if (var == ATTN_AUTO) {
+      attn_variant chosen = ATTN_AUTO;
+      s = measure(p, &chosen);
+      if (s != ATTN_OK) return s;
+      std::lock_guard<std::mutex> g(g_mu);
+      g_cache[key] = chosen;
+      return ATTN_OK;  // measure() left the chosen variant's outputs in place
+    }
+  }
+  return var == ATTN_FLASH ? run_flash(p) : run_pf(p);
+}
+
+attn_variant attn_select(int B, int H, int Nq, int Nk, int d, attn_dtype dt, void* stream) {
+  if (check_common(B, H, Nq, Nk, d, 1.f, dt) != ATTN_OK) return ATTN_AUTO;
+  const attn_variant forced = env_override();
+  if (forced != ATTN_AUTO) return forced;
+  Problem p = make(nullptr, nullptr, nullptr, nullptr, nullptr, B, H, Nq, Nk, d, 1.f / std::sqrt((float)d),
+                   dt, stream);
+  const Key key = key_of(p);
+  {
+    std::lock_guard<std::mutex> g(g_mu);
+    auto it = g_cache.find(key);
+    if (it != g_cache.end()) return it->second;
+  }
+  const size_t esz = dt == ATTN_F32 ? 4 : 2;
+  const size_t nq = (size_t)p.BH * Nq * d * esz, nk = (size_t)p.BH * Nk * d * esz;
+  void *bq = nullptr, *bk = nullptr, *bv = nullptr, *bo = nullptr, *bml = nullptr;
+  attn_variant chosen = ATTN_AUTO;
+  if (hipMalloc(&bq, nq) == hipSuccess && hipMalloc(&bk, nk) == hipSuccess && hipMalloc(&bv, nk) == hipSuccess &&
+      hipMalloc(&bo, nq) == hipSuccess && hipMalloc(&bml, (size_t)p.BH * Nq * 2 * sizeof(float)) == hipSuccess &&
+      hipMemsetAsync(bq, 0, nq, p.stream) == hipSuccess && hipMemsetAsync(bk, 0, nk, p.stream) == hipSuccess &&
+      hipMemsetAsync(bv, 0, nk, p.stream) == hipSuccess) {
+    p.q = bq;
+    p.k = bk;
+    p.v = bv;
+    p.out = bo;
+    p.ml = (float*)bml;
+    if (measure(p, &chosen) != ATTN_OK) chosen = ATTN_AUTO;
+    (void)hipStreamSynchronize(p.stream);
+  }
+  (void)hipFree(bq);
+  (void)hipFree(bk);
+  (void)hipFree(bv);
+  (void)hipFree(bo);
+  (void)hipFree(bml);
+  if (chosen != ATTN_AUTO) {
+    std::lock_guard<std::mutex> g(g_mu);
+    g_cache[key] = chosen;
+  }
+  return chosen;
+}
+
+void attn_select_reset(void) {
+  std::lock_guard<std::mutex> g(g_mu);
+  g_cache.clear();
+}
+
+}  // extern "C"

@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Throughput of the SD UNet attention hot path on one MI355X.
+
+One step = one full attention forward (attn_forward with the variant the
+per-shape selector picks, i.e. every kernel of the chosen form) over the
+seeded synthetic inputs of the SD 512x512 top-level self-attention
+(B=2, H=8, Nq=Nk=4096, d=40, fp16), inputs already resident in HBM.
+
+Prints ONE JSON line with the headline metric (useful attention TFLOP/s,
+4*B*H*Nq*Nk*d per step, and its fraction of the fp16 dense MFMA peak), the
+roofline record of the dominant kernel (HIP-event durations of that kernel's
+launches inside the timed region), and the CPU oracle timed on a bounded
+sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+                    [--variant auto|pf|flash] [--no-cpu-baseline]
+                    [--configs-out FILE]   # also time every config, write JSONL there
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s + % fp16 MFMA peak @ B=2,H=8,N=4096,d=40"
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}  # dense MFMA (fp16/bf16); fp32 vector
+HBM_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "attention_attn_stats_amd", "csrc", "attn_mfma.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, if it was taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(f"{kernel}@{workload}")
+    if not e or e.get("kernel_src_sha256_16") != kernel_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def device_inputs(cfg):
+    import torch
+    from attention_attn_stats_amd import synth
+    q, k, v = cfg.inputs()
+    conv = {"f16": lambda a: torch.from_numpy(a), "f32": lambda a: torch.from_numpy(a),
+            "bf16": lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16)}[cfg.dtype]
+    del synth
+    return [conv(x).cuda().contiguous() for x in (q, k, v)]
+
+
+def time_config(cfg, variant: str, steps: int, warmup: int):
+    """Time `steps` forwards; returns a dict with per-step and per-kernel times."""
+    import torch
+    import attention_attn_stats_amd as attn
+    q, k, v = device_inputs(cfg)
+    out = torch.empty_like(q)
+    ml = torch.empty((cfg.B, cfg.H, cfg.Nq, 2), device=q.device, dtype=torch.float32)
+    stream = torch.cuda.current_stream()
+    # the selector decides (and caches) on the first call; the chosen form is
+    # then issued kernel by kernel so that each kernel gets its own events
+    attn.forward(q, k, v, variant=variant, out=out, ml=ml, scale=cfg.scale)
+    chosen = variant if variant != "auto" else attn.select(cfg.B, cfg.H, cfg.Nq, cfg.Nk, cfg.d,
+                                                           q.dtype)
+
+    def step(evs=None):
+        if chosen == "flash":
+            if evs:
+                evs[0].record(stream)
+            attn.flash(q, k, v, out=out, ml=ml, scale=cfg.scale)
+            if evs:
+                evs[1].record(stream)
+        else:
+            if evs:
+                evs[0].record(stream)
+            attn.stats(q, k, ml=ml, scale=cfg.scale)
+            if evs:
+                evs[1].record(stream)
+            attn.pv(q, k, v, ml, out=out, scale=cfg.scale)
+            if evs:
+                evs[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    nev = 2 if chosen == "flash" else 3
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = {}
+    if chosen == "flash":
+        kern["flash"] = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    else:
+        kern["stats"] = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+        kern["pv"] = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    return {"variant": chosen, "ms_per_step": wall * 1e3 / steps, "kernel_ms": kern}
+
+
+def cpu_baseline(cfg, budget_s: float = 12.0):
+    """The float64 oracle on a bounded sample of the workload: whole heads
+    (all Nq query rows against all Nk keys), as many as fit the budget."""
+    import numpy as np
+    import oracle
+    from attention_attn_stats_amd import synth
+    threads = min(16, os.cpu_count() or 1)
+    q, k, v = (synth.widen(x, cfg.dtype).reshape(cfg.B * cfg.H, -1, cfg.d) for x in cfg.inputs())
+    t0 = time.perf_counter()
+    oracle.attention(q[:1], k[:1], v[:1], cfg.scale, nthreads=threads)
+    t1 = time.perf_counter() - t0
+    heads = int(max(1, min(cfg.B * cfg.H - 1, budget_s / max(t1, 1e-3) - 1)))
+    t0 = time.perf_counter()
+    oracle.attention(q[1:1 + heads], k[1:1 + heads], v[1:1 + heads], cfg.scale, nthreads=threads)
+    t = time.perf_counter() - t0
+    flops = 4.0 * heads * cfg.Nq * cfg.Nk * cfg.d
+    del np
+    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} of the {cfg.B * cfg.H} heads of {cfg.name} (each {cfg.Nq} queries x "
+                      f"{cfg.Nk} keys x d={cfg.d}, float64 with the score matrix materialised), "
+                      f"{t:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="sd512_self")
+    ap.add_argument("--variant", default="auto", choices=["auto", "pf", "flash"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--configs-out", default=None)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this attention path is not sharded across GPUs "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from attention_attn_stats_amd.configs import CONFIGS
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    cfg = CONFIGS[args.config]
+    r = time_config(cfg, args.variant, args.steps, args.warmup)
+    flops = cfg.flops
+    tflops = flops / (r["ms_per_step"] * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[cfg.dtype]
+    # dominant kernel: the one with the largest share of the step
+    kname, kms = max(r["kernel_ms"].items(), key=lambda kv: kv[1])
+    if kname == "stats":
+        kflops = 2.0 * cfg.B * cfg.H * cfg.Nq * cfg.Nk * cfg.d  # Q K^T only
+    else:
+        kflops = float(flops)  # flash and pv both do Q K^T and P V (pv recomputes Q K^T)
+    achieved = kflops / (kms * 1e-3) / 1e12
+    kernel_id = {"flash": "attn_flash", "stats": "attn_stats", "pv": "attn_pv"}[kname]
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": load_traffic(kernel_id, cfg.name),
+            "kernel": kernel_id, "kernel_ms": round(kms, 5)}
+    line = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "Nq": cfg.Nq, "Nk": cfg.Nk, "d": cfg.d,
+                   "variant": r["variant"], "parallelism": "single GPU"},
+        "pct_fp16_mfma_peak": round(100.0 * tflops / PEAK_TFLOPS["f16"], 2),
+        "kernel_ms": {k_: round(v_, 5) for k_, v_ in r["kernel_ms"].items()},
+        "roofline": roof,
+    }
+    if args.configs_out:
+        with open(args.configs_out, "w") as f:
+            for name, c in CONFIGS.items():
+                for var in ("pf", "flash"):
+                    rr = time_config(c, var, max(20, args.steps // 4), 5)
+                    t = c.flops / (rr["ms_per_step"] * 1e-3) / 1e12
+                    rec = {"config": name, "variant": var, "dtype": c.dtype, "ms_per_step": rr["ms_per_step"],
+                           "kernel_ms": rr["kernel_ms"], "tflops": t,
+                           "pct_peak": 100 * t / PEAK_TFLOPS[c.dtype]}
+                    f.write(json.dumps(rec) + "\n")
+                    log(json.dumps(rec))
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

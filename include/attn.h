@@ -39,7 +39,9 @@
  * and is complete when that stream is; buffers must stay valid until then.
  *
  * Supported: d in {40, 80, 160}; dt in {ATTN_F32, ATTN_F16, ATTN_BF16};
- * any B, H, Nq, Nk >= 1 with B*H*max(Nq,Nk)*d < 2^31 elements per tensor.
+ * any B, H, Nq, Nk >= 1 with B*H*max(Nq,Nk)*d < 2^31 elements per tensor;
+ * scale finite and > 0 (the usual 1/sqrt(d) softmax temperature).  q, k, v,
+ * out must be 16-byte aligned and ml 8-byte aligned.
  * F16/BF16 run on the matrix cores with float32 accumulation and float32
  * softmax state; F32 is a vector-ALU float32 path kept for exactness checks.
  *
@@ -56,8 +58,9 @@ extern "C" {
 
 typedef enum {
   ATTN_OK = 0,
-  ATTN_ERR_INVALID_ARG = 1, /* null required pointer, dimension < 1, non-finite
-                               scale, tensor larger than 2^31 - 1 elements */
+  ATTN_ERR_INVALID_ARG = 1, /* null required pointer, pointer not 16-byte
+                               aligned (ml: 8-byte), dimension < 1, scale not
+                               finite and > 0, tensor of 2^31 or more elements */
   ATTN_ERR_UNSUPPORTED = 2, /* d not in {40, 80, 160}, unknown dtype/variant */
   ATTN_ERR_HIP = 3          /* the HIP runtime reported an error */
 } attn_status;
