@@ -5,8 +5,10 @@
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -21,20 +23,72 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",
     # never emit packed fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in ordinary VGPRs (the softmax reads them on the VALU)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    # no NaN operands are expected (IEEE max would otherwise quiet every input first)
+    "-fno-honor-nans",
     "-I", INCLUDE, "-I", CSRC,
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libattn.so next to this file; returns its path."""
+_MFMA_OP = re.compile(r"^\s*(v_mfma_\S+)")
+# MFMA opcodes whose VGPR-form code (accumulator in ordinary VGPRs, chains
+# issued back to back, destination allowed to overlap the accumulator input)
+# has been checked on gfx950 hardware.  A build that emits any other MFMA
+# opcode stops here instead of shipping unverified code: an older-generation
+# 16x16x16 op mixed into such chains produced wrong sums.
+VERIFIED_MFMA = {"v_mfma_f32_16x16x32_f16", "v_mfma_f32_16x16x32_bf16",
+                 "v_mfma_f32_32x32x16_f16", "v_mfma_f32_32x32x16_bf16"}
+# For these the ISA forbids a destination that partially overlaps the
+# accumulator input (the assembler rejects it); the compiled code is checked.
+NO_PARTIAL_OVERLAP = {"v_mfma_f32_32x32x16_f16", "v_mfma_f32_32x32x16_bf16"}
+_MFMA_REGS = re.compile(r"^\s*(v_mfma_\S+)\s+v\[(\d+):(\d+)\],\s*\S+,\s*\S+,\s*v\[(\d+):(\d+)\]")
+
+
+def unverified_mfma(asm_text: str) -> list:
+    """MFMA instructions outside VERIFIED_MFMA in the device assembly."""
+    bad = []
+    for line in asm_text.splitlines():
+        m = _MFMA_OP.match(line)
+        if m and m.group(1) not in VERIFIED_MFMA:
+            bad.append(line.strip())
+        r = _MFMA_REGS.match(line)
+        if r and r.group(1) in NO_PARTIAL_OVERLAP:
+            d0, d1, c0, c1 = (int(r.group(i)) for i in (2, 3, 4, 5))
+            if (d0, d1) != (c0, c1) and not (d1 < c0 or c1 < d0):
+                bad.append(line.strip() + "    <- partial dst/srcC overlap")
+    return bad
+
+
+def verify_device_code(hipcc: str, verbose: bool = False, defines=()) -> None:
+    """Compile the matrix-core source to gfx950 assembly and reject unverified MFMA opcodes."""
+    with tempfile.TemporaryDirectory() as td:
+        asm = os.path.join(td, "attn_mfma.s")
+        cmd = [hipcc, *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-x", "hip", "--cuda-device-only", "-S",
+               os.path.join(CSRC, "attn_mfma.hip"), "-o", asm]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("device assembly generation failed:\n" + r.stderr)
+        text = open(asm).read()
+    bad = unverified_mfma(text)
+    if bad:
+        raise RuntimeError("unverified MFMA opcodes in device code:\n" + "\n".join(bad[:10]))
+    if verbose:
+        print(f"verified {text.count('v_mfma_')} MFMA instructions are all of {sorted(VERIFIED_MFMA)}")
+
+
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile every source and link libattn.so (or `out`) ; returns its path.
+    `defines` are extra -D settings of the kernels' compile-time tuning knobs."""
     hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
-    objdir = os.path.join(HERE, "_build")
+    objdir = os.path.join(HERE, "_build", os.path.basename(out))
     os.makedirs(objdir, exist_ok=True)
     objs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
-        cmd = [hipcc, *HIPCC_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *HIPCC_FLAGS, *[f"-D{d}" for d in defines], *lang, "-c",
+               os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -46,13 +100,14 @@ def build(verbose: bool = False) -> str:
         if verbose and msg.strip():
             print(msg)
         objs.append(obj)
-    tmp = LIB + ".tmp"
+    verify_device_code(hipcc, verbose, defines)
+    tmp = out + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

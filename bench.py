@@ -120,26 +120,30 @@ def time_config(cfg, variant: str, steps: int, warmup: int):
 
 
 def cpu_baseline(cfg, budget_s: float = 12.0):
-    """The float64 oracle on a bounded sample of the workload: whole heads
-    (all Nq query rows against all Nk keys), as many as fit the budget."""
-    import numpy as np
+    """The float64 oracle timed on a bounded sample of the workload: whole
+    heads (all Nq query rows against all Nk keys), as many passes over the
+    heads as fill about `budget_s` seconds of wall time."""
     import oracle
     from attention_attn_stats_amd import synth
     threads = min(16, os.cpu_count() or 1)
-    q, k, v = (synth.widen(x, cfg.dtype).reshape(cfg.B * cfg.H, -1, cfg.d) for x in cfg.inputs())
+    bh = cfg.B * cfg.H
+    q, k, v = (synth.widen(x, cfg.dtype).reshape(bh, -1, cfg.d) for x in cfg.inputs())
     t0 = time.perf_counter()
     oracle.attention(q[:1], k[:1], v[:1], cfg.scale, nthreads=threads)
-    t1 = time.perf_counter() - t0
-    heads = int(max(1, min(cfg.B * cfg.H - 1, budget_s / max(t1, 1e-3) - 1)))
+    per_head = max(time.perf_counter() - t0, 1e-3)
+    heads = int(min(60 * bh, max(1, budget_s / per_head)))
+    done = 0
     t0 = time.perf_counter()
-    oracle.attention(q[1:1 + heads], k[1:1 + heads], v[1:1 + heads], cfg.scale, nthreads=threads)
+    while done < heads:
+        n = min(bh, heads - done)
+        oracle.attention(q[:n], k[:n], v[:n], cfg.scale, nthreads=threads)
+        done += n
     t = time.perf_counter() - t0
-    flops = 4.0 * heads * cfg.Nq * cfg.Nk * cfg.d
-    del np
+    flops = 4.0 * done * cfg.Nq * cfg.Nk * cfg.d
     return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{heads} of the {cfg.B * cfg.H} heads of {cfg.name} (each {cfg.Nq} queries x "
-                      f"{cfg.Nk} keys x d={cfg.d}, float64 with the score matrix materialised), "
-                      f"{t:.1f} s wall"}
+            "sample": f"{done} head evaluations ({done / bh:.1f} passes over the {bh} heads of {cfg.name}; "
+                      f"each {cfg.Nq} queries x {cfg.Nk} keys x d={cfg.d}, float64, score matrix "
+                      f"materialised), {t:.1f} s wall"}
 
 
 def main():
@@ -151,7 +155,20 @@ def main():
     ap.add_argument("--variant", default="auto", choices=["auto", "pf", "flash"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--configs-out", default=None)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes 5 times (calibrates the "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+    if args.copy_probe:
+        import torch
+        n = args.copy_probe // 4
+        src = torch.ones(n, device="cuda", dtype=torch.float32)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n * 4, "launches": 5}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this attention path is not sharded across GPUs "
               "(run with --gpus 1)", file=sys.stderr)
