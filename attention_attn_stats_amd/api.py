@@ -95,7 +95,9 @@ def flash(q, k, v, out=None, ml=None, want_ml=False, scale=None):
 
 
 def forward(q, k, v, variant="auto", out=None, ml=None, scale=None):
-    """Attention with the given variant ('auto', 'pf', 'flash'); returns (out, ml)."""
+    """Attention with the given variant ('auto', 'pf', 'flash'); returns (out, ml).
+    ml holds the row statistics when the partially fused form ran and is
+    untouched scratch when the single pass ran (use flash(..., want_ml=True))."""
     B, H, Nq, Nk, d = _dims(q, k, v)
     out = torch.empty_like(q) if out is None else out
     ml = _ml_for(q, ml)

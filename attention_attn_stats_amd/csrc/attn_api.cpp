@@ -105,11 +105,14 @@ attn_status time_variant(const Problem& p, attn_variant var, int iters, float* m
     (void)hipEventDestroy(e0);
     return ATTN_ERR_HIP;
   }
-  attn_status st = var == ATTN_FLASH ? run_flash(p) : run_pf(p);
+  Problem pf = p;
+  pf.ml = nullptr;  // the single pass runs without the statistics output, as attn_forward issues it
+  auto run = [&]() { return var == ATTN_FLASH ? run_flash(pf) : run_pf(p); };
+  attn_status st = run();
   float times[100];
   for (int i = 0; i < iters && st == ATTN_OK; ++i) {
     if (hipEventRecord(e0, p.stream) != hipSuccess) st = ATTN_ERR_HIP;
-    if (st == ATTN_OK) st = var == ATTN_FLASH ? run_flash(p) : run_pf(p);
+    if (st == ATTN_OK) st = run();
     if (st == ATTN_OK && hipEventRecord(e1, p.stream) != hipSuccess) st = ATTN_ERR_HIP;
     if (st == ATTN_OK && hipEventSynchronize(e1) != hipSuccess) st = ATTN_ERR_HIP;
     if (st == ATTN_OK && hipEventElapsedTime(&times[i], e0, e1) != hipSuccess) st = ATTN_ERR_HIP;
@@ -211,7 +214,12 @@ attn_status attn_forward(const void* q, const void* k, const void* v, void* out,
       return ATTN_OK;  // measure() left the chosen variant's outputs in place
     }
   }
-  return var == ATTN_FLASH ? run_flash(p) : run_pf(p);
+  if (var == ATTN_FLASH) {
+    Problem pf = p;
+    pf.ml = nullptr;  // the single pass needs no statistics buffer
+    return run_flash(pf);
+  }
+  return run_pf(p);
 }
 
 attn_variant attn_select(int B, int H, int Nq, int Nk, int d, attn_dtype dt, void* stream) {

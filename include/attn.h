@@ -101,9 +101,10 @@ attn_status attn_flash(const void* q, const void* k, const void* v, void* out, f
                        int B, int H, int Nq, int Nk, int d, float scale, attn_dtype dt,
                        void* stream);
 
-/* Full forward.  ATTN_PARTIAL_FUSED runs attn_stats then attn_pv (two
- * launches) and needs `ml` as scratch/output; ATTN_FLASH runs attn_flash and
- * writes `ml` if it is non-NULL; ATTN_AUTO uses the cached choice for this
+/* Full forward: computes `out`.  ATTN_PARTIAL_FUSED runs attn_stats then
+ * attn_pv (two launches) and needs `ml` (it then holds the statistics);
+ * ATTN_FLASH runs attn_flash without statistics output, `ml` is not touched
+ * (call attn_flash with ml_out to get them); ATTN_AUTO uses the cached choice for this
  * shape, and on the first call for a shape times both variants on the
  * caller's buffers (synchronising `stream` once) before caching the winner
  * (if `ml` is NULL only FLASH is eligible).  The environment variable
