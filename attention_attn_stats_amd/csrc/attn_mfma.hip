@@ -155,7 +155,8 @@ __device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
 //
 // One workgroup = 8 waves = 4 query groups of 32 queries x 2 key halves; the
 // two waves of a query group walk alternate 32-key blocks (the key range is
-// split in two, as in the block-split reduction) and merge their partial
+// split in two, as in the block-split reduction; 64-key blocks at d = 40,
+// 32 otherwise) and merge their partial
 // (m, l, O) through LDS at the end.  K and V blocks go through a ring of LDS
 // slots per key half, filled cooperatively by that half's waves.
 //
@@ -181,7 +182,6 @@ constexpr int kT = 64 * kW;         // threads per workgroup
 constexpr int kHT = 64 * kQG;       // threads per key half
 constexpr int kQ = 32;              // queries per wave
 constexpr int kQWG = kQG * kQ;      // queries per workgroup
-constexpr int kBN = 32;             // keys per block
 
 template <int D>
 struct Shape {
@@ -195,10 +195,12 @@ struct Shape {
   // padding columns 40..47 in both.
   static constexpr int PK = D == 40 ? 56 : D + 8;
   static constexpr int PV = D == 40 ? 48 : (D == 80 ? 80 : D + 16);
+  static constexpr int BN = D == 40 ? 64 : 32;   // keys per block
+  static constexpr int NT = BN / 32;             // 32-key score tiles per block
   static constexpr int NBUF = D >= 160 ? 2 : 3;  // ring slots per key half
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
-  static constexpr int NLD = (kBN * CPR + kHT - 1) / kHT;
-  static constexpr int SLOT = kBN * (PK + PV);   // 16-bit elements per slot (K then V)
+  static constexpr int NLD = (BN * CPR + kHT - 1) / kHT;
+  static constexpr int SLOT = BN * (PK + PV);    // 16-bit elements per slot (K then V)
   static constexpr int NEX = 2 * MT * 4 + 8;     // floats per lane handed over in the merge
   static constexpr int RING = 2 * NBUF * SLOT;   // 16-bit elements, both halves
   static constexpr int SMEM = RING > NEX * 64 * kQG * 2 ? RING : NEX * 64 * kQG * 2;
@@ -214,6 +216,7 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
                                                  int qtiles, int nwg, float scale) {
   using S = Shape<D>;
   constexpr int KS = S::KS, MT = S::MT, PK = S::PK, PV = S::PV, NBUF = S::NBUF, NEX = S::NEX;
+  constexpr int BN = S::BN, NT = S::NT;
   // Fold scale and max subtraction into the MFMA (fp16, d with a spare dim).
   // Not when (m, l) is reported: the pre-scaled Q perturbs the scores by up to
   // a few 1e-4 of their exp2 value, too close to the 1e-3 bound on l.
@@ -238,13 +241,13 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
   if constexpr (S::kOnes) {
     // padding columns of every slot of this half: K column D = 1.0 (the
     // max-subtraction dim), V column D = 1.0 (the row-sum dim), zero elsewhere
-    for (int e = htid; e < NBUF * kBN * (PK - D); e += kHT) {
+    for (int e = htid; e < NBUF * BN * (PK - D); e += kHT) {
       const int r = e / (PK - D), col = e - r * (PK - D);
-      ring[(r / kBN) * S::SLOT + (r % kBN) * PK + D + col] = (kFold && col == 0) ? TR::kOne : (uint16_t)0;
+      ring[(r / BN) * S::SLOT + (r % BN) * PK + D + col] = (kFold && col == 0) ? TR::kOne : (uint16_t)0;
     }
-    for (int e = htid; e < NBUF * kBN * (PV - D); e += kHT) {
+    for (int e = htid; e < NBUF * BN * (PV - D); e += kHT) {
       const int r = e / (PV - D), col = e - r * (PV - D);
-      ring[(r / kBN) * S::SLOT + kBN * PK + (r % kBN) * PV + D + col] = col == 0 ? TR::kOne : (uint16_t)0;
+      ring[(r / BN) * S::SLOT + BN * PK + (r % BN) * PV + D + col] = col == 0 ? TR::kOne : (uint16_t)0;
     }
   }
 
@@ -299,17 +302,17 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
     for (int mt = 0; mt < MT; ++mt) o[qt][mt] = (f4v){0.f, 0.f, 0.f, 0.f};
   float mtrue = -INFINITY, lsum = 0.f;
 
-  const int nblk = (Nk + kBN - 1) / kBN;
+  const int nblk = (Nk + BN - 1) / BN;
   const int niter = (nblk + 1) / 2;
   // staging of this half's block for iteration `it` (key block 2 it + half)
   uint4 kst[S::NLD], vst[S::NLD];
   auto gload = [&](int it) {
-    const int key0 = (2 * it + half) * kBN;
+    const int key0 = (2 * it + half) * BN;
 #pragma unroll
     for (int r = 0; r < S::NLD; ++r) {
       const int ch = htid + r * kHT;
       const int row = ch / S::CPR, col = (ch - row * S::CPR) * 8;
-      const bool ok = ch < kBN * S::CPR && key0 + row < Nk;
+      const bool ok = ch < BN * S::CPR && key0 + row < Nk;
       const size_t off = (size_t)(ok ? key0 + row : 0) * D + (ok ? col : 0);
       uint4 kx = *(const uint4*)(kh + off);
       uint4 vx = *(const uint4*)(vh + off);
@@ -319,11 +322,11 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
   };
   auto swrite = [&](int slot) {
     uint16_t* ks_ = ring + slot * S::SLOT;
-    uint16_t* vs_ = ks_ + kBN * PK;
+    uint16_t* vs_ = ks_ + BN * PK;
 #pragma unroll
     for (int r = 0; r < S::NLD; ++r) {
       const int ch = htid + r * kHT;
-      if (ch < kBN * S::CPR) {
+      if (ch < BN * S::CPR) {
         const int row = ch / S::CPR, col = (ch - row * S::CPR) * 8;
         *(uint4*)(ks_ + row * PK + col) = kst[r];
         *(uint4*)(vs_ + row * PV + col) = vst[r];
@@ -351,31 +354,40 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
     const int kb = 2 * it + half;
     if (kb < nblk) {
       const uint16_t* Ks = ring + (it % NBUF) * S::SLOT;
-      const uint16_t* Vs = Ks + kBN * PK;
-      // ---- scores in exp2 units, 32 keys x 32 queries (the folded form already has -mref)
-      f16v x = {};
+      const uint16_t* Vs = Ks + BN * PK;
+      // ---- scores in exp2 units, NT tiles of 32 keys x 32 queries (the
+      // folded form already has -mref)
+      f16v x[NT];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int d0 = ks * 16 + hi * 8;
-        const s8v a = *(const s8v*)(Ks + l32 * PK + ((kFold || d0 < D) ? d0 : D - 8));
-        x = TR::mma32(a, qf[ks], x);
+      for (int t = 0; t < NT; ++t) {
+        x[t] = (f16v){};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int d0 = ks * 16 + hi * 8;
+          const s8v a = *(const s8v*)(Ks + (t * 32 + l32) * PK + ((kFold || d0 < D) ? d0 : D - 8));
+          x[t] = TR::mma32(a, qf[ks], x[t]);
+        }
+        if constexpr (!kFold) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) x[t][i] = __builtin_fmaf(x[t][i], c, -mref);
+        }
       }
-      if constexpr (!kFold) {
+      if (kb * BN + BN > Nk) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = __builtin_fmaf(x[i], c, -mref);
-      }
-      if (kb * kBN + kBN > Nk) {
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (kb * kBN + (i / 4) * 8 + hi * 4 + (i % 4) >= Nk) x[i] = -INFINITY;
+          for (int i = 0; i < 16; ++i)
+            if (kb * BN + t * 32 + (i / 4) * 8 + hi * 4 + (i % 4) >= Nk) x[t][i] = -INFINITY;
       }
       // ---- online softmax.  The reference max moves only when the block max
       // exceeds it by more than 2^8, so exp2(x) <= 256 stays exact in 16-bit P
       // and fp32 sums; O / l does not depend on the reference value.
       if constexpr (MODE != kModePV) {
-        float bm = x[0];
+        float bm = x[0][0];
 #pragma unroll
-        for (int i = 1; i < 16; ++i) bm = __builtin_fmaxf(bm, x[i]);
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) bm = __builtin_fmaxf(bm, x[t][i]);
         bm = pair_max32(bm);
         mtrue = __builtin_fmaxf(mtrue, bm + mref);
         if (__any(bm > 8.f) || it == 0) {
@@ -387,7 +399,9 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
           set_fold(mref);
           lsum *= alpha;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) x[i] -= delta;
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x[t][i] -= delta;
 #pragma unroll
           for (int qt = 0; qt < 2; ++qt) {
             const float ao = __shfl(alpha, qt * 16 + li);
@@ -396,33 +410,37 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
           }
         }
       }
-      float p[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(x[i]);
-      if constexpr (kValuSum) {
-        float ls = 0.f;
+      for (int t = 0; t < NT; ++t) {
+        float p[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) ls += p[i];
-        lsum += ls;
-      }
-      uint32_t pa[4], pb[4];
+        for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(x[t][i]);
+        if constexpr (kValuSum) {
+          float ls = 0.f;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        pa[d] = TR::pack2(p[2 * d], p[2 * d + 1]);
-        pb[d] = TR::pack2(p[8 + 2 * d], p[8 + 2 * d + 1]);
-        swap16(pa[d], pb[d]);  // pa: queries 0-15, pb: queries 16-31
-      }
-      const s8v P0 = __builtin_bit_cast(s8v, (uint4){pa[0], pa[1], pa[2], pa[3]});
-      const s8v P1 = __builtin_bit_cast(s8v, (uint4){pb[0], pb[1], pb[2], pb[3]});
-      // ---- O^T += V^T P^T; lane (G, li) supplies V^T[dim 16 mt + li][keys vbase + {0..3}, vbase + 8 + {0..3}]
+          for (int i = 0; i < 16; ++i) ls += p[i];
+          lsum += ls;
+        }
+        uint32_t pa[4], pb[4];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const uint16_t* va = Vs + (vbase + (li >> 2)) * PV + mt * 16 + 4 * (li & 3);
-        const s4v v0 = lds_read_tr16(va);
-        const s4v v1 = lds_read_tr16(va + 8 * PV);
-        const s8v vop = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        o[0][mt] = TR::mma16(vop, P0, o[0][mt]);
-        o[1][mt] = TR::mma16(vop, P1, o[1][mt]);
+        for (int d = 0; d < 4; ++d) {
+          pa[d] = TR::pack2(p[2 * d], p[2 * d + 1]);
+          pb[d] = TR::pack2(p[8 + 2 * d], p[8 + 2 * d + 1]);
+          swap16(pa[d], pb[d]);  // pa: queries 0-15, pb: queries 16-31
+        }
+        const s8v P0 = __builtin_bit_cast(s8v, (uint4){pa[0], pa[1], pa[2], pa[3]});
+        const s8v P1 = __builtin_bit_cast(s8v, (uint4){pb[0], pb[1], pb[2], pb[3]});
+        // ---- O^T += V^T P^T; lane (G, li) supplies V^T[dim 16 mt + li][keys vbase + {0..3}, vbase + 8 + {0..3}]
+        const uint16_t* Vt = Vs + t * 32 * PV;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const uint16_t* va = Vt + (vbase + (li >> 2)) * PV + mt * 16 + 4 * (li & 3);
+          const s4v v0 = lds_read_tr16(va);
+          const s4v v1 = lds_read_tr16(va + 8 * PV);
+          const s8v vop = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+          o[0][mt] = TR::mma16(vop, P0, o[0][mt]);
+          o[1][mt] = TR::mma16(vop, P1, o[1][mt]);
+        }
       }
     }
     if (it + NBUF - 1 < niter) swrite((it + NBUF - 1) % NBUF);
