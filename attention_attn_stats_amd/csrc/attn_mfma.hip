@@ -87,6 +87,15 @@ constexpr int kModePV = 2;       // softmax from given (m, l), O only
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their no-wait maxima)
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Raw buffer resource over `bytes` bytes at p (stride 0): loads at offsets
+// at or past `bytes` return zero without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rs, int voff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
+}
+
 typedef uint16_t __attribute__((address_space(3))) lds_u16;
 
 __device__ __forceinline__ s4v lds_read_tr16(const uint16_t* p) {
@@ -304,20 +313,29 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
 
   const int nblk = (Nk + BN - 1) / BN;
   const int niter = (nblk + 1) / 2;
-  // staging of this half's block for iteration `it` (key block 2 it + half)
+  // staging of this half's block for iteration `it` (key block 2 it + half).
+  // Buffer loads over a resource that starts at the block's first key and
+  // ends at key Nk: each lane's offset inside the block is fixed, the block
+  // address is scalar work, and rows past Nk come back as zeros from the
+  // hardware range check.
+  const int halfu = __builtin_amdgcn_readfirstlane(half);
+  int loff[S::NLD];
+#pragma unroll
+  for (int r = 0; r < S::NLD; ++r) {
+    const int ch = htid + r * kHT;
+    const int row = ch / S::CPR, col = (ch - row * S::CPR) * 8;
+    loff[r] = ch < BN * S::CPR ? (row * D + col) * 2 : 0;
+  }
   uint4 kst[S::NLD], vst[S::NLD];
   auto gload = [&](int it) {
-    const int key0 = (2 * it + half) * BN;
+    const int key0 = (2 * it + halfu) * BN;
+    const int bytes = (Nk > key0 ? Nk - key0 : 0) * D * 2;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kh + (size_t)key0 * D, bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vh + (size_t)key0 * D, bytes);
 #pragma unroll
     for (int r = 0; r < S::NLD; ++r) {
-      const int ch = htid + r * kHT;
-      const int row = ch / S::CPR, col = (ch - row * S::CPR) * 8;
-      const bool ok = ch < BN * S::CPR && key0 + row < Nk;
-      const size_t off = (size_t)(ok ? key0 + row : 0) * D + (ok ? col : 0);
-      uint4 kx = *(const uint4*)(kh + off);
-      uint4 vx = *(const uint4*)(vh + off);
-      kst[r] = ok ? kx : make_uint4(0, 0, 0, 0);
-      vst[r] = ok ? vx : make_uint4(0, 0, 0, 0);
+      kst[r] = load16(krs, loff[r]);
+      vst[r] = load16(vrs, loff[r]);
     }
   };
   auto swrite = [&](int slot) {
