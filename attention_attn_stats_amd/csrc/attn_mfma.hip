@@ -59,6 +59,8 @@ struct F16 {
   // exp2 value, about the size of the rounding of P itself: Q may be
   // pre-scaled where only O is produced.
   static constexpr bool kPrescaleOk = true;
+  // packed 16-bit max instructions exist for this type
+  static constexpr bool kPackedMax = true;
 };
 
 struct BF16 {
@@ -78,11 +80,21 @@ struct BF16 {
   static constexpr bool kRoundedSumOk = false;
   // ... and for pre-scaling Q: the scale stays in an fp32 FMA.
   static constexpr bool kPrescaleOk = false;
+  static constexpr bool kPackedMax = false;
 };
 
 constexpr int kModeFlash = 0;    // online softmax, O only
 constexpr int kModeFlashML = 1;  // online softmax, O and (m, l)
 constexpr int kModePV = 2;       // softmax from given (m, l), O only
+
+// max of two pairs of non-negative fp16 values (v_pk_maximum3_f16 from chains)
+__device__ __forceinline__ uint32_t pmax(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_maximum(__builtin_bit_cast(h2v, a), __builtin_bit_cast(h2v, b)));
+}
+__device__ __forceinline__ float pmax_halves(uint32_t a) {
+  const h2v v = __builtin_bit_cast(h2v, a);
+  return (float)__builtin_elementwise_maximum(v[0], v[1]);
+}
 
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their no-wait maxima)
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -185,6 +197,11 @@ __device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
 //   * d = 40 pads the PV product to 48 rows; LDS column 40 of V holds 1.0 so
 //     row 40 of O^T is the row sum l of the same rounded P.
 // ---------------------------------------------------------------------------
+// LDS row of key k of a V block (an involution): keys 16-19 and 20-23 (and
+// their copies in every 32-key tile) trade places, so that the 8 rows one
+// ds_read_b64_tr_b16 takes per half wave fall in distinct LDS banks.
+__device__ __forceinline__ int vrow(int k) { return k ^ (((k >> 4) & 1) << 2); }
+
 constexpr int kQG = 4;              // query groups per workgroup
 constexpr int kW = 2 * kQG;         // waves per workgroup (x 2 key halves)
 constexpr int kT = 64 * kW;         // threads per workgroup
@@ -198,17 +215,17 @@ struct Shape {
   static constexpr int MT = (D + 15) / 16;      // 16-row tiles of O^T
   static constexpr bool kOnes = (D % 16) != 0;  // LDS column D of V holds 1.0 -> O^T row D = l
   static constexpr bool kSpareDim = (D % 16) == 8;  // the last K step has a spare dim D
-  // LDS row pitches (16-bit elements): K rows are read 32 consecutive rows at
-  // a time (pitch = 4 * odd words); V is read by ds_read_b64_tr_b16 as 4 rows
-  // x 32 bytes per 16 lanes (pitch mod 32 words in {8, 24}); d = 40 needs
-  // padding columns 40..47 in both.
+  // LDS row pitches (16-bit elements), chosen with bank-conflict counters:
+  // K rows are read 32 consecutive rows at a time by ds_read_b128 (pitch of
+  // 20 or 28 words mod 64 reads in one pass); V rows by ds_read_b64_tr_b16 as
+  // 4 rows x 32 bytes per 16 lanes (pitch of 24 or 40 words mod 64, with the
+  // vrow permutation); d = 40 needs padding columns 40..47 in both.
   static constexpr int PK = D == 40 ? 56 : D + 8;
   static constexpr int PV = D == 40 ? 48 : (D == 80 ? 80 : D + 16);
   static constexpr int BN = D == 40 ? 64 : 32;   // keys per block
   static constexpr int NT = BN / 32;             // 32-key score tiles per block
   static constexpr int NBUF = D >= 160 ? 2 : 3;  // ring slots per key half
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
-  static constexpr int NLD = (BN * CPR + kHT - 1) / kHT;
   static constexpr int SLOT = BN * (PK + PV);    // 16-bit elements per slot (K then V)
   static constexpr int NEX = 2 * MT * 4 + 8;     // floats per lane handed over in the merge
   static constexpr int RING = 2 * NBUF * SLOT;   // 16-bit elements, both halves
@@ -231,6 +248,8 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
   // a few 1e-4 of their exp2 value, too close to the 1e-3 bound on l.
   constexpr bool kFold = S::kSpareDim && TR::kPrescaleOk && MODE != kModeFlashML;
   constexpr bool kValuSum = MODE != kModePV && (!S::kOnes || (MODE == kModeFlashML && !TR::kRoundedSumOk));
+  // fp16 flash without (m, l) out: the rescale test runs on the packed P
+  constexpr bool kLazyMax = TR::kPackedMax && MODE == kModeFlash;
   __shared__ __attribute__((aligned(16))) uint16_t smem[S::SMEM];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -313,43 +332,54 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
 
   const int nblk = (Nk + BN - 1) / BN;
   const int niter = (nblk + 1) / 2;
-  // staging of this half's block for iteration `it` (key block 2 it + half).
-  // Buffer loads over a resource that starts at the block's first key and
-  // ends at key Nk: each lane's offset inside the block is fixed, the block
-  // address is scalar work, and rows past Nk come back as zeros from the
-  // hardware range check.
+  // Staging of this half's block for iteration `it` (key block 2 it + half).
+  // One job = one 16-byte chunk per lane, one buffer load and one
+  // ds_write_b128 per wave; the half's waves take jobs qg, qg + 4, ...  K
+  // chunks go column by column (lane -> key row), V chunks in LDS order over
+  // the permuted key rows; both orders write LDS without bank conflicts.  The
+  // buffer resource starts at the block's first key and ends at key Nk, so
+  // the block address is scalar work and rows past Nk come back as zeros.
+  constexpr int VCH = PV / 8;                                 // chunks per V row (incl. padding)
+  constexpr int KJOBS = BN * S::CPR / 64, NJOB = KJOBS + (BN * VCH + 63) / 64;
+  constexpr int JPW = (NJOB + kQG - 1) / kQG;                 // jobs per wave
+  static_assert(BN * S::CPR % 64 == 0, "K staging covers whole waves");
   const int halfu = __builtin_amdgcn_readfirstlane(half);
-  int loff[S::NLD];
+  const int qgu = __builtin_amdgcn_readfirstlane(qg);
+  int goff[JPW], soff[JPW];  // byte offset in the block (< 0: no chunk), element offset in the slot
 #pragma unroll
-  for (int r = 0; r < S::NLD; ++r) {
-    const int ch = htid + r * kHT;
-    const int row = ch / S::CPR, col = (ch - row * S::CPR) * 8;
-    loff[r] = ch < BN * S::CPR ? (row * D + col) * 2 : 0;
+  for (int r = 0; r < JPW; ++r) {
+    const int j = qgu + kQG * r;
+    goff[r] = -1;
+    soff[r] = 0;
+    if (j < KJOBS) {
+      const int qi = 64 * j + lane, col = qi / BN, row = qi - col * BN;
+      goff[r] = (row * D + col * 8) * 2;
+      soff[r] = row * PK + col * 8;
+    } else if (j < NJOB) {
+      const int qi = 64 * (j - KJOBS) + lane, row = qi / VCH, col = qi - row * VCH;
+      if (row < BN && col < S::CPR) {
+        goff[r] = (vrow(row) * D + col * 8) * 2;
+        soff[r] = BN * PK + row * PV + col * 8;
+      }
+    }
   }
-  uint4 kst[S::NLD], vst[S::NLD];
+  uint4 stg[JPW];
   auto gload = [&](int it) {
     const int key0 = (2 * it + halfu) * BN;
     const int bytes = (Nk > key0 ? Nk - key0 : 0) * D * 2;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(kh + (size_t)key0 * D, bytes);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vh + (size_t)key0 * D, bytes);
 #pragma unroll
-    for (int r = 0; r < S::NLD; ++r) {
-      kst[r] = load16(krs, loff[r]);
-      vst[r] = load16(vrs, loff[r]);
+    for (int r = 0; r < JPW; ++r) {
+      const int j = qgu + kQG * r;
+      if (j < NJOB) stg[r] = load16(j < KJOBS ? krs : vrs, goff[r] < 0 ? 0x7FFFFFF0 : goff[r]);
     }
   };
   auto swrite = [&](int slot) {
-    uint16_t* ks_ = ring + slot * S::SLOT;
-    uint16_t* vs_ = ks_ + BN * PK;
+    uint16_t* sl = ring + slot * S::SLOT;
 #pragma unroll
-    for (int r = 0; r < S::NLD; ++r) {
-      const int ch = htid + r * kHT;
-      if (ch < BN * S::CPR) {
-        const int row = ch / S::CPR, col = (ch - row * S::CPR) * 8;
-        *(uint4*)(ks_ + row * PK + col) = kst[r];
-        *(uint4*)(vs_ + row * PV + col) = vst[r];
-      }
-    }
+    for (int r = 0; r < JPW; ++r)
+      if (qgu + kQG * r < NJOB && goff[r] >= 0) *(uint4*)(sl + soff[r]) = stg[r];
   };
 
 #pragma unroll
@@ -365,11 +395,68 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
   __syncthreads();
   if (NBUF - 1 < niter) gload(NBUF - 1);
 
-  // key order after the row swap: lane group G holds keys vbase + {0..3} and vbase + 8 + {0..3}
-  const int vbase = (G & 1) * 16 + (G >> 1) * 4;
+  // key order after the row swap: lane group G holds keys vbase + {0..3} and
+  // vbase + 8 + {0..3}, at LDS rows vrow(vbase) + {0..3}, + 8 + {0..3}
+  const int vbase = vrow((G & 1) * 16 + (G >> 1) * 4);
+
+  // Online softmax.  The reference max moves only when a block's scores
+  // exceed it by more than 8 (exp2 units), so P = exp2(x) <= 256 stays exact
+  // in 16-bit P and in the fp32 sums; O / l does not depend on the reference.
+  // move the reference to the running max (16-bit rounded when folded),
+  // rescale O and l, and shift the block's scores
+  auto rebase = [&](f16v (&x)[NT], float bm) {
+    mtrue = __builtin_fmaxf(mtrue, bm + mref);
+    const float mnew = kFold ? TR::lo(TR::pack2(mtrue, 0.f)) : mtrue;
+    const float delta = mnew - mref;
+    const float alpha = __builtin_amdgcn_exp2f(-delta);
+    mref = mnew;
+    set_fold(mref);
+    lsum *= alpha;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[t][i] -= delta;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const float ao = __shfl(alpha, qt * 16 + li);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) o[qt][mt] *= ao;
+    }
+  };
+  auto block_max = [&](const f16v (&x)[NT]) {
+    float bm = x[0][0];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) bm = __builtin_fmaxf(bm, x[t][i]);
+    return pair_max32(bm);  // both lanes of a query
+  };
+  // P = exp2(x) rounded to 16 bits, re-laid out for the PV product:
+  // pa[t]: queries 0-15, pb[t]: queries 16-31; returns the fp32 sum of P
+  uint32_t pa[NT][4], pb[NT][4];
+  auto expand = [&](const f16v (&x)[NT]) {
+    float ls = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float p[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(x[t][i]);
+      if constexpr (kValuSum) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ls += p[i];
+      }
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        pa[t][d] = TR::pack2(p[2 * d], p[2 * d + 1]);
+        pb[t][d] = TR::pack2(p[8 + 2 * d], p[8 + 2 * d + 1]);
+        swap16(pa[t][d], pb[t][d]);
+      }
+    }
+    return ls;
+  };
 
   for (int it = 0; it < niter; ++it) {
-    const int kb = 2 * it + half;
+    const int kb = 2 * it + halfu;  // wave-uniform
     if (kb < nblk) {
       const uint16_t* Ks = ring + (it % NBUF) * S::SLOT;
       const uint16_t* Vs = Ks + BN * PK;
@@ -397,58 +484,35 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
           for (int i = 0; i < 16; ++i)
             if (kb * BN + t * 32 + (i / 4) * 8 + hi * 4 + (i % 4) >= Nk) x[t][i] = -INFINITY;
       }
-      // ---- online softmax.  The reference max moves only when the block max
-      // exceeds it by more than 2^8, so exp2(x) <= 256 stays exact in 16-bit P
-      // and fp32 sums; O / l does not depend on the reference value.
-      if constexpr (MODE != kModePV) {
-        float bm = x[0][0];
+      float ls;
+      if constexpr (kLazyMax) {
+        // exponentials first: the 16-bit P themselves tell whether a score
+        // passed mref + 8 (P > 256); only then is the block max taken and P
+        // formed again against the new reference
+        ls = expand(x);
+        uint32_t mw = pa[0][0];
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) bm = __builtin_fmaxf(bm, x[t][i]);
-        bm = pair_max32(bm);
-        mtrue = __builtin_fmaxf(mtrue, bm + mref);
-        if (__any(bm > 8.f) || it == 0) {
-          // new reference: the running max, rounded to 16 bits when folded
-          const float mnew = kFold ? TR::lo(TR::pack2(mtrue, 0.f)) : mtrue;
-          const float delta = mnew - mref;
-          const float alpha = __builtin_amdgcn_exp2f(-delta);
-          mref = mnew;
-          set_fold(mref);
-          lsum *= alpha;
-#pragma unroll
-          for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) x[t][i] -= delta;
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt) {
-            const float ao = __shfl(alpha, qt * 16 + li);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) o[qt][mt] *= ao;
-          }
+          for (int d = 0; d < 4; ++d) mw = pmax(pmax(mw, pa[t][d]), pb[t][d]);
+        if (__any(pmax_halves(mw) > 256.f) || it == 0) {
+          rebase(x, block_max(x));
+          ls = expand(x);
         }
+      } else {
+        if constexpr (MODE != kModePV) {
+          const float bm = block_max(x);
+          if (__any(bm > 8.f) || it == 0) rebase(x, bm);
+          else mtrue = __builtin_fmaxf(mtrue, bm + mref);
+        }
+        ls = expand(x);
       }
+      if constexpr (kValuSum) lsum += ls;
+      // ---- O^T += V^T P^T; lane (G, li) supplies V^T[dim 16 mt + li][its 8 keys]
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        float p[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(x[t][i]);
-        if constexpr (kValuSum) {
-          float ls = 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) ls += p[i];
-          lsum += ls;
-        }
-        uint32_t pa[4], pb[4];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          pa[d] = TR::pack2(p[2 * d], p[2 * d + 1]);
-          pb[d] = TR::pack2(p[8 + 2 * d], p[8 + 2 * d + 1]);
-          swap16(pa[d], pb[d]);  // pa: queries 0-15, pb: queries 16-31
-        }
-        const s8v P0 = __builtin_bit_cast(s8v, (uint4){pa[0], pa[1], pa[2], pa[3]});
-        const s8v P1 = __builtin_bit_cast(s8v, (uint4){pb[0], pb[1], pb[2], pb[3]});
-        // ---- O^T += V^T P^T; lane (G, li) supplies V^T[dim 16 mt + li][keys vbase + {0..3}, vbase + 8 + {0..3}]
+        const s8v P0 = __builtin_bit_cast(s8v, (uint4){pa[t][0], pa[t][1], pa[t][2], pa[t][3]});
+        const s8v P1 = __builtin_bit_cast(s8v, (uint4){pb[t][0], pb[t][1], pb[t][2], pb[t][3]});
         const uint16_t* Vt = Vs + t * 32 * PV;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
