@@ -463,6 +463,9 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
       // ---- scores in exp2 units, NT tiles of 32 keys x 32 queries (the
       // folded form already has -mref)
       f16v x[NT];
+      // raised wave priority while issuing matrix work, so that a wave with
+      // MFMAs ready goes first and the others' vector work fills the gaps
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         x[t] = (f16v){};
@@ -477,6 +480,7 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
           for (int i = 0; i < 16; ++i) x[t][i] = __builtin_fmaf(x[t][i], c, -mref);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       if (kb * BN + BN > Nk) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -509,6 +513,7 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
       }
       if constexpr (kValuSum) lsum += ls;
       // ---- O^T += V^T P^T; lane (G, li) supplies V^T[dim 16 mt + li][its 8 keys]
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const s8v P0 = __builtin_bit_cast(s8v, (uint4){pa[t][0], pa[t][1], pa[t][2], pa[t][3]});
@@ -525,6 +530,7 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (it + NBUF - 1 < niter) swrite((it + NBUF - 1) % NBUF);
     __syncthreads();
     if (it + NBUF < niter) gload(it + NBUF);
