@@ -4,11 +4,11 @@
 // Method: "Speed Is All You Need: On-Device Acceleration of Large Diffusion
 // Models via GPU-Aware Optimizations" (Chen et al.), news write-up, section on
 // improving attention efficiency.  Two forms of O = softmax(scale Q K^T) V:
-//   * partially fused softmax: stats_kernel reduces every row of
-//     A = scale Q K^T to (m, l) -- the N x 2 tensor -- with the row's keys cut
-//     into blocks that are reduced separately and merged in the same launch;
-//     fwd_kernel<.., kModePV> then applies the softmax inside the product with
-//     V.  A is recomputed from Q and K on chip, never stored.
+//   * partially fused softmax: fwd_kernel<.., kModeStats> reduces every row
+//     of A = scale Q K^T to (m, l) -- the N x 2 tensor -- with the row's keys
+//     cut into blocks that are reduced separately and merged in the same
+//     launch; fwd_kernel<.., kModePV> then applies the softmax inside the
+//     product with V.  A is recomputed from Q and K on chip, never stored.
 //   * FlashAttention: fwd_kernel<.., kModeFlash*> walks the key blocks once
 //     with a running max and running sum (exact online softmax).
 // Exponentials are exp2 with scale * log2(e) folded in; (m, l) are reported
@@ -86,6 +86,7 @@ struct BF16 {
 constexpr int kModeFlash = 0;    // online softmax, O only
 constexpr int kModeFlashML = 1;  // online softmax, O and (m, l)
 constexpr int kModePV = 2;       // softmax from given (m, l), O only
+constexpr int kModeStats = 3;    // (m, l) only: the first pass of the partially fused form
 
 // max of two pairs of non-negative fp16 values (v_pk_maximum3_f16 from chains)
 __device__ __forceinline__ uint32_t pmax(uint32_t a, uint32_t b) {
@@ -227,9 +228,6 @@ struct Shape {
   static constexpr int NBUF = D >= 160 ? 2 : 3;  // ring slots per key half
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
   static constexpr int SLOT = BN * (PK + PV);    // 16-bit elements per slot (K then V)
-  static constexpr int NEX = 2 * MT * 4 + 8;     // floats per lane handed over in the merge
-  static constexpr int RING = 2 * NBUF * SLOT;   // 16-bit elements, both halves
-  static constexpr int SMEM = RING > NEX * 64 * kQG * 2 ? RING : NEX * 64 * kQG * 2;
   static_assert(D % 8 == 0 && D >= 16, "head dim must be a multiple of 8");
 };
 
@@ -241,16 +239,29 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
                                                  float* __restrict__ ml, int Nq, int Nk,
                                                  int qtiles, int nwg, float scale) {
   using S = Shape<D>;
-  constexpr int KS = S::KS, MT = S::MT, PK = S::PK, PV = S::PV, NBUF = S::NBUF, NEX = S::NEX;
+  constexpr int KS = S::KS, MT = S::MT, PK = S::PK, PV = S::PV, NBUF = S::NBUF;
   constexpr int BN = S::BN, NT = S::NT;
   // Fold scale and max subtraction into the MFMA (fp16, d with a spare dim).
   // Not when (m, l) is reported: the pre-scaled Q perturbs the scores by up to
   // a few 1e-4 of their exp2 value, too close to the 1e-3 bound on l.
-  constexpr bool kFold = S::kSpareDim && TR::kPrescaleOk && MODE != kModeFlashML;
-  constexpr bool kValuSum = MODE != kModePV && (!S::kOnes || (MODE == kModeFlashML && !TR::kRoundedSumOk));
+  constexpr bool kStats = MODE == kModeStats;
+  constexpr bool kReportML = MODE == kModeFlashML || kStats;
+  constexpr bool kFold = S::kSpareDim && TR::kPrescaleOk && !kReportML;
+  // where l comes from: the matrix cores (V's ones column in the flash forms,
+  // a ones operand in the stats form) or fp32 sums on the vector ALU
+  constexpr bool kValuSum = MODE != kModePV && (kStats ? !TR::kRoundedSumOk
+                                                       : (!S::kOnes || (kReportML && !TR::kRoundedSumOk)));
+  constexpr int MO = kStats ? 1 : MT;  // 16-row tiles of the accumulator (stats: the row sums)
+  // floats per lane handed from one key half to the other in the merge: O
+  // (not in the stats form), then 4 per query tile
+  constexpr int XO = kStats ? 0 : 2 * MT * 4, NEX = XO + 8;
+  // LDS slot: the K block, then the V block (none in the stats form)
+  constexpr int SLOT = kStats ? BN * PK : S::SLOT;
+  constexpr int RING = 2 * NBUF * SLOT, XCH = NEX * 64 * kQG * 2;
+  constexpr int SMEM = RING > XCH ? RING : XCH;
   // fp16 flash without (m, l) out: the rescale test runs on the packed P
   constexpr bool kLazyMax = TR::kPackedMax && MODE == kModeFlash;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[S::SMEM];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int qg = wave % kQG, half = wave / kQG, htid = tid % kHT;
@@ -263,19 +274,19 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
   const int qbase = (tile - head * qtiles) * kQWG + qg * kQ;
   const uint16_t* qh = q + (size_t)head * Nq * D;
   const uint16_t* kh = k + (size_t)head * Nk * D;
-  const uint16_t* vh = v + (size_t)head * Nk * D;
-  uint16_t* const ring = smem + half * NBUF * S::SLOT;
+  const uint16_t* vh = kStats ? nullptr : v + (size_t)head * Nk * D;  // the stats form reads no V
+  uint16_t* const ring = smem + half * NBUF * SLOT;
 
   if constexpr (S::kOnes) {
     // padding columns of every slot of this half: K column D = 1.0 (the
     // max-subtraction dim), V column D = 1.0 (the row-sum dim), zero elsewhere
     for (int e = htid; e < NBUF * BN * (PK - D); e += kHT) {
       const int r = e / (PK - D), col = e - r * (PK - D);
-      ring[(r / BN) * S::SLOT + (r % BN) * PK + D + col] = (kFold && col == 0) ? TR::kOne : (uint16_t)0;
+      ring[(r / BN) * SLOT + (r % BN) * PK + D + col] = (kFold && col == 0) ? TR::kOne : (uint16_t)0;
     }
-    for (int e = htid; e < NBUF * BN * (PV - D); e += kHT) {
+    for (int e = htid; !kStats && e < NBUF * BN * (PV - D); e += kHT) {
       const int r = e / (PV - D), col = e - r * (PV - D);
-      ring[(r / BN) * S::SLOT + BN * PK + (r % BN) * PV + D + col] = col == 0 ? TR::kOne : (uint16_t)0;
+      ring[(r / BN) * SLOT + BN * PK + (r % BN) * PV + D + col] = col == 0 ? TR::kOne : (uint16_t)0;
     }
   }
 
@@ -323,11 +334,11 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
   if (MODE == kModePV) set_fold(mref);
 
   // state: O in the 16x16 layout; the max in exp2 units in the 32x32 layout
-  f4v o[2][MT];
+  f4v o[2][MO];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) o[qt][mt] = (f4v){0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MO; ++mt) o[qt][mt] = (f4v){0.f, 0.f, 0.f, 0.f};
   float mtrue = -INFINITY, lsum = 0.f;
 
   const int nblk = (Nk + BN - 1) / BN;
@@ -340,7 +351,7 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
   // buffer resource starts at the block's first key and ends at key Nk, so
   // the block address is scalar work and rows past Nk come back as zeros.
   constexpr int VCH = PV / 8;                                 // chunks per V row (incl. padding)
-  constexpr int KJOBS = BN * S::CPR / 64, NJOB = KJOBS + (BN * VCH + 63) / 64;
+  constexpr int KJOBS = BN * S::CPR / 64, NJOB = KJOBS + (kStats ? 0 : (BN * VCH + 63) / 64);
   constexpr int JPW = (NJOB + kQG - 1) / kQG;                 // jobs per wave
   static_assert(BN * S::CPR % 64 == 0, "K staging covers whole waves");
   const int halfu = __builtin_amdgcn_readfirstlane(half);
@@ -376,7 +387,7 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
     }
   };
   auto swrite = [&](int slot) {
-    uint16_t* sl = ring + slot * S::SLOT;
+    uint16_t* sl = ring + slot * SLOT;
 #pragma unroll
     for (int r = 0; r < JPW; ++r)
       if (qgu + kQG * r < NJOB && goff[r] >= 0) *(uint4*)(sl + soff[r]) = stg[r];
@@ -420,7 +431,7 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
     for (int qt = 0; qt < 2; ++qt) {
       const float ao = __shfl(alpha, qt * 16 + li);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) o[qt][mt] *= ao;
+      for (int mt = 0; mt < MO; ++mt) o[qt][mt] *= ao;
     }
   };
   auto block_max = [&](const f16v (&x)[NT]) {
@@ -458,7 +469,7 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
   for (int it = 0; it < niter; ++it) {
     const int kb = 2 * it + halfu;  // wave-uniform
     if (kb < nblk) {
-      const uint16_t* Ks = ring + (it % NBUF) * S::SLOT;
+      const uint16_t* Ks = ring + (it % NBUF) * SLOT;
       const uint16_t* Vs = Ks + BN * PK;
       // ---- scores in exp2 units, NT tiles of 32 keys x 32 queries (the
       // folded form already has -mref)
@@ -512,12 +523,23 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
         ls = expand(x);
       }
       if constexpr (kValuSum) lsum += ls;
-      // ---- O^T += V^T P^T; lane (G, li) supplies V^T[dim 16 mt + li][its 8 keys]
+      // ---- O^T += V^T P^T; lane (G, li) supplies V^T[dim 16 mt + li][its 8 keys].
+      // The stats form multiplies by a ones operand instead: every row of the
+      // 16x16 result is then the per-query sum of the tile's rounded P.
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const s8v P0 = __builtin_bit_cast(s8v, (uint4){pa[t][0], pa[t][1], pa[t][2], pa[t][3]});
         const s8v P1 = __builtin_bit_cast(s8v, (uint4){pb[t][0], pb[t][1], pb[t][2], pb[t][3]});
+        if constexpr (kStats) {
+          if constexpr (!kValuSum) {
+            const short one = (short)TR::kOne;
+            const s8v ones = {one, one, one, one, one, one, one, one};
+            o[0][0] = TR::mma16(ones, P0, o[0][0]);
+            o[1][0] = TR::mma16(ones, P1, o[1][0]);
+          }
+          continue;
+        }
         const uint16_t* Vt = Vs + t * 32 * PV;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -548,7 +570,9 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
       lo[qt] = 0.f;
       lro[qt] = 0.f;
     } else {
-      if constexpr (S::kOnes) {
+      if constexpr (kStats && !kValuSum) {
+        lo[qt] = o[qt][0][0];  // all rows of the ones product are equal
+      } else if constexpr (S::kOnes && !kStats) {
         constexpr int GL = (D % 16) / 4, IL = D % 4;
         lo[qt] = __shfl(o[qt][MT - 1][IL], GL * 16 + li);
       } else {
@@ -564,23 +588,23 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < (kStats ? 0 : MT); ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) ex[((qt * MT + mt) * 4 + i) * 64] = o[qt][mt][i];
-      ex[(2 * MT * 4 + qt * 4 + 0) * 64] = mo[qt];
-      ex[(2 * MT * 4 + qt * 4 + 1) * 64] = mto[qt];
-      ex[(2 * MT * 4 + qt * 4 + 2) * 64] = lo[qt];
-      ex[(2 * MT * 4 + qt * 4 + 3) * 64] = lro[qt];
+      ex[(XO + qt * 4 + 0) * 64] = mo[qt];
+      ex[(XO + qt * 4 + 1) * 64] = mto[qt];
+      ex[(XO + qt * 4 + 2) * 64] = lo[qt];
+      ex[(XO + qt * 4 + 3) * 64] = lro[qt];
     }
   }
   __syncthreads();
   if (half == 1) return;
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
-    const float mB = ex[(2 * MT * 4 + qt * 4 + 0) * 64];
-    const float mtB = ex[(2 * MT * 4 + qt * 4 + 1) * 64];
-    const float lB = ex[(2 * MT * 4 + qt * 4 + 2) * 64];
-    const float lrB = ex[(2 * MT * 4 + qt * 4 + 3) * 64];
+    const float mB = ex[(XO + qt * 4 + 0) * 64];
+    const float mtB = ex[(XO + qt * 4 + 1) * 64];
+    const float lB = ex[(XO + qt * 4 + 2) * 64];
+    const float lrB = ex[(XO + qt * 4 + 3) * 64];
     float fA = 1.f, fB = 1.f, M = mo[qt];
     if constexpr (MODE != kModePV) {
       // a half that saw no key holds (-inf, 0, 0) and contributes nothing
@@ -589,7 +613,7 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
       fB = __builtin_amdgcn_exp2f(mB - M);
     }
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < (kStats ? 0 : MT); ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[qt][mt][i] = o[qt][mt][i] * fA + ex[((qt * MT + mt) * 4 + i) * 64] * fB;
     const float l = lo[qt] * fA + lB * fB;
@@ -610,7 +634,7 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
     if (row < Nq) {
       uint16_t* op = out + ((size_t)head * Nq + row) * D;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+      for (int mt = 0; mt < (kStats ? 0 : MT); ++mt) {
         const int dim = mt * 16 + G * 4;
         if (dim < D) {
           uint2 w;
@@ -619,7 +643,7 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
           *(uint2*)(op + dim) = w;
         }
       }
-      if constexpr (MODE == kModeFlashML) {
+      if constexpr (kReportML) {
         if (G == 0) {
           // l was accumulated against the reference M; report it against the true max
           const float lt = lr * __builtin_amdgcn_exp2f(M - mt_all);
@@ -627,168 +651,6 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
         }
       }
     }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Stats kernel (partially fused softmax, pass 1).  One workgroup = 4 waves on
-// the same 64 queries of one head.  The row of A for each query is cut into
-// key blocks of 32; wave w reduces blocks w, w+4, w+8, ... to a running
-// (max, sum of exp) pair, and the four partial pairs are merged through LDS
-// with (m,l)+(m',l') = (M, l e^(m-M) + l' e^(m'-M)) before the single store.
-// K is read straight from global memory (L2) into MFMA operand registers.
-// ---------------------------------------------------------------------------
-constexpr int kSWaves = 4;           // waves per workgroup (stats kernel)
-constexpr int kSThreads = 64 * kSWaves;
-constexpr int kSQT = 4;              // 16-query tiles per workgroup
-constexpr int kSQ = 16 * kSQT;       // queries per workgroup (stats kernel)
-constexpr int kSBN = 32;             // keys per block (stats kernel)
-
-// The 16x16x32 MFMA covers the head dim in K=32 steps; a remainder of 8 or 16
-// dims takes one more step whose missing dims are zero in the Q operand and
-// read from a clamped, in-row K offset (finite data times zero).
-template <int D>
-struct SShape {
-  static constexpr int KS = D / 32;             // full K=32 steps
-  static constexpr int KR = D % 32;             // remainder dims: 0, 8 or 16
-  static constexpr int KRG = KR / 8;            // lane groups holding real remainder dims
-};
-template <int D>
-__device__ __forceinline__ int rem_off(int G) {
-  constexpr int KS = D / 32, KRG = (D % 32) / 8;
-  return KS * 32 + (G < KRG ? G : KRG - 1) * 8;
-}
-
-template <class TR, int D>
-__global__ __launch_bounds__(kSThreads) void stats_kernel(const uint16_t* __restrict__ q,
-                                                         const uint16_t* __restrict__ k,
-                                                         float* __restrict__ ml, int Nq, int Nk,
-                                                         int qtiles, int nwg, float scale) {
-  using S = SShape<D>;
-  constexpr int KS = S::KS, KR = S::KR;
-  constexpr int NKT = kSBN / 16;
-  __shared__ float part_m[kSWaves][kSQ];
-  __shared__ float part_l[kSWaves][kSQ];
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, G = lane >> 4, li = lane & 15;
-  const float c = scale * kLog2e;
-
-  const int tile = xcd_tile(nwg);
-  const int head = tile / qtiles;
-  const int qbase = (tile - head * qtiles) * kSQ;
-  const uint16_t* qh = q + (size_t)head * Nq * D;
-  const uint16_t* kh = k + (size_t)head * Nk * D;
-
-  s8v qf[kSQT][KS > 0 ? KS : 1];
-  s8v qr[kSQT];
-#pragma unroll
-  for (int qt = 0; qt < kSQT; ++qt) {
-    const int row = qbase + qt * 16 + li;
-    const bool ok = row < Nq;
-    const uint16_t* qp = qh + (size_t)(ok ? row : 0) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s8v x = *(const s8v*)(qp + ks * 32 + G * 8);
-      qf[qt][ks] = ok ? x : (s8v){0, 0, 0, 0, 0, 0, 0, 0};
-    }
-    if constexpr (KR != 0) {
-      s8v x = *(const s8v*)(qp + rem_off<D>(G));
-      qr[qt] = (ok && G < S::KRG) ? x : (s8v){0, 0, 0, 0, 0, 0, 0, 0};
-    }
-  }
-
-  float m[kSQT], l[kSQT];
-#pragma unroll
-  for (int qt = 0; qt < kSQT; ++qt) {
-    m[qt] = -INFINITY;
-    l[qt] = 0.f;
-  }
-
-  // K operand registers for one block: lane (G, li) holds key 16 kt + li,
-  // dims [32 ks + 8 G, +8) and the remainder dims.
-  s8v ka[NKT][KS > 0 ? KS : 1];
-  s8v kr8[NKT];
-  auto kload = [&](int kb) {
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-      const int key = kb * kSBN + kt * 16 + li;
-      const bool ok = key < Nk;
-      const uint16_t* kp = kh + (size_t)(ok ? key : 0) * D;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s8v x = *(const s8v*)(kp + ks * 32 + G * 8);
-        ka[kt][ks] = ok ? x : (s8v){0, 0, 0, 0, 0, 0, 0, 0};
-      }
-      if constexpr (KR != 0) {
-        s8v x = *(const s8v*)(kp + rem_off<D>(G));
-        kr8[kt] = ok ? x : (s8v){0, 0, 0, 0, 0, 0, 0, 0};
-      }
-    }
-  };
-
-  const int nblk = (Nk + kSBN - 1) / kSBN;
-  for (int kb = wave; kb < nblk; kb += kSWaves) {
-    kload(kb);
-#pragma unroll
-    for (int qt = 0; qt < kSQT; ++qt) {
-      f4v s[NKT];
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) {
-        s[kt] = (f4v){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) s[kt] = TR::mma16(ka[kt][ks], qf[qt][ks], s[kt]);
-        if constexpr (KR != 0) s[kt] = TR::mma16(kr8[kt], qr[qt], s[kt]);
-      }
-      if (kb * kSBN + kSBN > Nk) {
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (kb * kSBN + kt * 16 + G * 4 + i >= Nk) s[kt][i] = -INFINITY;
-      }
-      // block partial (bm, bl) merged into the running pair
-      float bm = s[0][0];
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bm = __builtin_fmaxf(bm, s[kt][i]);
-      bm = group_max(bm);
-      const float mn = __builtin_fmaxf(m[qt], bm);
-      const float mnc = mn * c;
-      float bl = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bl += __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], c, -mnc));
-      l[qt] = l[qt] * __builtin_amdgcn_exp2f((m[qt] - mn) * c) + bl;
-      m[qt] = mn;
-    }
-  }
-
-  // per-wave partial pairs: the four lane groups hold disjoint keys of the same query
-#pragma unroll
-  for (int qt = 0; qt < kSQT; ++qt) {
-    const float lw = group_sum(l[qt]);
-    if (G == 0) {
-      part_m[wave][qt * 16 + li] = m[qt];
-      part_l[wave][qt * 16 + li] = lw;
-    }
-  }
-  __syncthreads();
-  if (tid < kSQ) {
-    const int row = qbase + tid;
-    float M = part_m[0][tid];
-#pragma unroll
-    for (int w = 1; w < kSWaves; ++w) M = __builtin_fmaxf(M, part_m[w][tid]);
-    float L = 0.f;
-#pragma unroll
-    for (int w = 0; w < kSWaves; ++w) {
-      const float pm = part_m[w][tid];
-      // a wave that saw no key of this row holds (-inf, 0) and adds nothing
-      if (pm != -INFINITY) L += part_l[w][tid] * __builtin_amdgcn_exp2f((pm - M) * c);
-    }
-    if (row < Nq) *(float2*)(ml + ((size_t)head * Nq + row) * 2) = make_float2(M * scale, L);
   }
 }
 
@@ -800,17 +662,6 @@ hipError_t launch_fwd_t(const Problem& p) {
   hipLaunchKernelGGL((fwd_kernel<TR, D, MODE>), dim3((unsigned)nwg), dim3(kT), 0, p.stream,
                      (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v, (uint16_t*)p.out,
                      p.ml, p.Nq, p.Nk, qtiles, (int)nwg, p.scale);
-  return hipGetLastError();
-}
-
-template <class TR, int D>
-hipError_t launch_stats_t(const Problem& p) {
-  const int qtiles = (p.Nq + kSQ - 1) / kSQ;
-  const long long nwg = (long long)p.BH * qtiles;
-  if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((stats_kernel<TR, D>), dim3((unsigned)nwg), dim3(kSThreads), 0, p.stream,
-                     (const uint16_t*)p.q, (const uint16_t*)p.k, p.ml, p.Nq, p.Nk, qtiles, (int)nwg,
-                     p.scale);
   return hipGetLastError();
 }
 
@@ -828,7 +679,7 @@ hipError_t by_type(const Problem& p) {
   return p.dt == ATTN_BF16 ? by_dim<L, BF16>(p) : by_dim<L, F16>(p);
 }
 
-template <class TR, int D> struct StatsL { static hipError_t run(const Problem& p) { return launch_stats_t<TR, D>(p); } };
+template <class TR, int D> struct StatsL { static hipError_t run(const Problem& p) { return launch_fwd_t<TR, D, kModeStats>(p); } };
 template <class TR, int D> struct PvL { static hipError_t run(const Problem& p) { return launch_fwd_t<TR, D, kModePV>(p); } };
 template <class TR, int D> struct FlashL {
   static hipError_t run(const Problem& p) {
