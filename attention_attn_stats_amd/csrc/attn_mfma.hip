@@ -55,10 +55,6 @@ struct F16 {
   // A row sum of fp16-rounded P is within 2^-11 (relative) of the exact sum,
   // inside the 1e-3 bound on l, so the matrix-core ones-row sum may be reported.
   static constexpr bool kRoundedSumOk = true;
-  // Rounding c * q to fp16 perturbs a score by ~3e-4 (rms, relative) of its
-  // exp2 value, about the size of the rounding of P itself: Q may be
-  // pre-scaled where only O is produced.
-  static constexpr bool kPrescaleOk = true;
   // packed 16-bit max instructions exist for this type
   static constexpr bool kPackedMax = true;
 };
@@ -78,8 +74,6 @@ struct BF16 {
   static constexpr uint16_t kOne = 0x3F80;
   // bf16 rounding (2^-8) is too coarse for a reported l: sum in fp32 as well.
   static constexpr bool kRoundedSumOk = false;
-  // ... and for pre-scaling Q: the scale stays in an fp32 FMA.
-  static constexpr bool kPrescaleOk = false;
   static constexpr bool kPackedMax = false;
 };
 
@@ -185,11 +179,8 @@ __device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
 //   * S^T = K Q^T on 32x32x16 MFMAs: a 32-key x 32-query tile per block, the
 //     head dim in K=16 steps.  Lane l owns query l % 32 and 16 of the 32 keys;
 //     lanes l and l ^ 32 share a query.
-//   * fp16, d = 40: Q is pre-multiplied by c = scale * log2(e) and the last K
-//     step's spare dims are used: K's LDS column 40 holds 1.0 and Q's dim 40
-//     holds -m (the running reference max, rounded to 16 bits), so the MFMA
-//     returns c s - m and P = exp2(result) needs no vector-ALU arithmetic
-//     before the exponential.  Otherwise one FMA forms c s - m.
+//   * one fp32 FMA per score forms x = c s - m (c = scale * log2(e), m the
+//     reference max in exp2 units), and P = exp2(x).
 //   * P is rounded to 16 bits, and one v_permlane16_swap per pair of packed
 //     registers turns the 32x32 result layout into the B operands of two
 //     16x16x32 MFMAs (queries 0-15 and 16-31) for O^T += V^T P^T.  V^T comes
@@ -215,7 +206,6 @@ struct Shape {
   static constexpr int KS = (D + 15) / 16;      // K=16 steps of Q K^T
   static constexpr int MT = (D + 15) / 16;      // 16-row tiles of O^T
   static constexpr bool kOnes = (D % 16) != 0;  // LDS column D of V holds 1.0 -> O^T row D = l
-  static constexpr bool kSpareDim = (D % 16) == 8;  // the last K step has a spare dim D
   // LDS row pitches (16-bit elements), chosen with bank-conflict counters:
   // K rows are read 32 consecutive rows at a time by ds_read_b128 (pitch of
   // 20 or 28 words mod 64 reads in one pass); V rows by ds_read_b64_tr_b16 as
@@ -246,7 +236,6 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
   // a few 1e-4 of their exp2 value, too close to the 1e-3 bound on l.
   constexpr bool kStats = MODE == kModeStats;
   constexpr bool kReportML = MODE == kModeFlashML || kStats;
-  constexpr bool kFold = S::kSpareDim && TR::kPrescaleOk && !kReportML;
   // where l comes from: the matrix cores (V's ones column in the flash forms,
   // a ones operand in the stats form) or fp32 sums on the vector ALU
   constexpr bool kValuSum = MODE != kModePV && (kStats ? !TR::kRoundedSumOk
@@ -278,11 +267,11 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
   uint16_t* const ring = smem + half * NBUF * SLOT;
 
   if constexpr (S::kOnes) {
-    // padding columns of every slot of this half: K column D = 1.0 (the
-    // max-subtraction dim), V column D = 1.0 (the row-sum dim), zero elsewhere
+    // padding columns of every slot of this half: zero, except V column D =
+    // 1.0 (the row-sum dim)
     for (int e = htid; e < NBUF * BN * (PK - D); e += kHT) {
       const int r = e / (PK - D), col = e - r * (PK - D);
-      ring[(r / BN) * SLOT + (r % BN) * PK + D + col] = (kFold && col == 0) ? TR::kOne : (uint16_t)0;
+      ring[(r / BN) * SLOT + (r % BN) * PK + D + col] = 0;
     }
     for (int e = htid; !kStats && e < NBUF * BN * (PV - D); e += kHT) {
       const int r = e / (PV - D), col = e - r * (PV - D);
@@ -291,16 +280,17 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
   }
 
   // Reference max in exp2 units, per query (lane l32): the value subtracted
-  // from every score (by the folded MFMA as a 16-bit value, else in fp32).
-  // The online form starts from 0 and always re-bases on its first block.
+  // (in fp32) from every score.  The online form starts from 0 and always
+  // re-bases on its first block.
   float mref = 0.f;
   if constexpr (MODE == kModePV) {
     const int row = qbase + l32;
-    const float m = row < Nq ? ml[((size_t)head * Nq + row) * 2] * kLog2e : 0.f;  // stored in natural units
-    mref = kFold ? TR::lo(TR::pack2(m, 0.f)) : m;
+    mref = row < Nq ? ml[((size_t)head * Nq + row) * 2] * kLog2e : 0.f;  // stored in natural units
   }
   // Q operand (B of the 32x32x16 MFMA): query l32, dims [16 ks + 8 hi, +8),
-  // zero past d; pre-multiplied by c when folding (the folded dim d = -mref).
+  // zero past d.  The scale stays out of the 16-bit operand: rounding c * q
+  // to 16 bits would move a score by up to 2^-11 of its own size, which is
+  // visible in P once scores reach tens.
   s8v qf[KS];
   {
     const int row = qbase + l32;
@@ -310,29 +300,9 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
     for (int ks = 0; ks < KS; ++ks) {
       const int d0 = ks * 16 + hi * 8;
       const uint4 x = *(const uint4*)(qp + (d0 < D ? d0 : D - 8));
-      uint32_t w[4] = {x.x, x.y, x.z, x.w};
-      if constexpr (kFold) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = TR::pack2(TR::lo(w[j]) * c, TR::hi(w[j]) * c);
-      }
-      qf[ks] = (ok && d0 < D) ? __builtin_bit_cast(s8v, (uint4){w[0], w[1], w[2], w[3]})
-                              : (s8v){0, 0, 0, 0, 0, 0, 0, 0};
+      qf[ks] = (ok && d0 < D) ? __builtin_bit_cast(s8v, x) : (s8v){0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
-  // the folded dim lives in element 0 of the last K step's operand in lanes hi = 1
-  auto set_fold = [&](float m) {
-    if constexpr (kFold) {
-      if (hi == 1) {
-        uint32_t w0 = __builtin_bit_cast(uint4, qf[KS - 1]).x;
-        w0 = (w0 & 0xFFFF0000u) | (TR::pack2(-m, 0.f) & 0xFFFFu);
-        uint4 u = __builtin_bit_cast(uint4, qf[KS - 1]);
-        u.x = w0;
-        qf[KS - 1] = __builtin_bit_cast(s8v, u);
-      }
-    }
-  };
-  if (MODE == kModePV) set_fold(mref);
-
   // state: O in the 16x16 layout; the max in exp2 units in the 32x32 layout
   f4v o[2][MO];
 #pragma unroll
@@ -413,15 +383,13 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
   // Online softmax.  The reference max moves only when a block's scores
   // exceed it by more than 8 (exp2 units), so P = exp2(x) <= 256 stays exact
   // in 16-bit P and in the fp32 sums; O / l does not depend on the reference.
-  // move the reference to the running max (16-bit rounded when folded),
-  // rescale O and l, and shift the block's scores
+  // move the reference to the running max, rescale O and l, and shift the
+  // block's scores
   auto rebase = [&](f16v (&x)[NT], float bm) {
     mtrue = __builtin_fmaxf(mtrue, bm + mref);
-    const float mnew = kFold ? TR::lo(TR::pack2(mtrue, 0.f)) : mtrue;
-    const float delta = mnew - mref;
+    const float delta = mtrue - mref;
     const float alpha = __builtin_amdgcn_exp2f(-delta);
-    mref = mnew;
-    set_fold(mref);
+    mref = mtrue;
     lsum *= alpha;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -471,8 +439,7 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
     if (kb < nblk) {
       const uint16_t* Ks = ring + (it % NBUF) * SLOT;
       const uint16_t* Vs = Ks + BN * PK;
-      // ---- scores in exp2 units, NT tiles of 32 keys x 32 queries (the
-      // folded form already has -mref)
+      // ---- scores in exp2 units relative to mref, NT tiles of 32 keys x 32 queries
       f16v x[NT];
       // raised wave priority while issuing matrix work, so that a wave with
       // MFMAs ready goes first and the others' vector work fills the gaps
@@ -483,13 +450,12 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const int d0 = ks * 16 + hi * 8;
-          const s8v a = *(const s8v*)(Ks + (t * 32 + l32) * PK + ((kFold || d0 < D) ? d0 : D - 8));
+          // past d the LDS padding is zero (and so is Q)
+          const s8v a = *(const s8v*)(Ks + (t * 32 + l32) * PK + d0);
           x[t] = TR::mma32(a, qf[ks], x[t]);
         }
-        if constexpr (!kFold) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) x[t][i] = __builtin_fmaf(x[t][i], c, -mref);
-        }
+        for (int i = 0; i < 16; ++i) x[t][i] = __builtin_fmaf(x[t][i], c, -mref);
       }
       __builtin_amdgcn_s_setprio(0);
       if (kb * BN + BN > Nk) {
@@ -623,8 +589,8 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
     float inv = 0.f;
     if (row < Nq) {
       if constexpr (MODE == kModePV) {
-        // P was formed against mref (the given m, rounded when folded); the
-        // given l is relative to the given m
+        // P was formed against mref = the given m (M here); the given l is
+        // relative to it
         const float2 st = *(const float2*)(ml + ((size_t)head * Nq + row) * 2);
         inv = __builtin_amdgcn_exp2f(M - st.x * kLog2e) / st.y;
       } else {

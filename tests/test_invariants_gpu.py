@@ -1,0 +1,171 @@
+"""GPU properties of the attention path that hold at any size, checked through
+the C ABI on inputs built to exercise one behaviour each:
+
+* the softmax weights of a row sum to one: a V whose every row is the same
+  vector gives that vector back, and Q = 0 gives the column means of V with
+  m = 0 and l = Nk;
+* adding one vector u to every key adds scale * q.u to a whole score row,
+  which moves m by that amount and leaves O and l unchanged;
+* one key far above the rest takes (almost) all the weight, wherever it sits
+  in the key sequence (late keys force a rescale of the running state);
+* scores that grow along the key sequence make the running max move on every
+  block; the result still matches the oracle;
+* results are bitwise repeatable, and the same on a side stream as on the
+  default stream.
+"""
+import numpy as np
+import pytest
+
+from attention_attn_stats_amd import synth
+from attention_attn_stats_amd.configs import CONFIGS
+from gpu_util import assert_close_ml, assert_close_o, from_device, reference, to_device
+
+pytestmark = pytest.mark.gpu
+
+FORMS = ("pf", "flash")
+
+
+def _forward(q, k, v, form, scale):
+    import attention_attn_stats_amd as attn
+    if form == "pf":
+        ml = attn.stats(q, k, scale=scale)
+        return attn.pv(q, k, v, ml, scale=scale), ml
+    return attn.flash(q, k, v, want_ml=True, scale=scale)
+
+
+def _exact(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Round to the element type and back to float64 (the values the GPU sees)."""
+    return synth.widen(synth.round_to(a, dtype), dtype)
+
+
+@pytest.mark.parametrize("form", FORMS)
+@pytest.mark.parametrize("dtype,d", [("f16", 40), ("bf16", 80), ("f16", 160)])
+def test_constant_v_rows_come_back(form, dtype, d):
+    B, H, Nq, Nk = 1, 2, 150, 333
+    q = synth.round_to(synth.normal(11, B * H * Nq * d).reshape(B, H, Nq, d), dtype)
+    k = synth.round_to(synth.normal(12, B * H * Nk * d).reshape(B, H, Nk, d), dtype)
+    row = synth.normal(13, d) * 2.0
+    v = synth.round_to(np.broadcast_to(row, (B, H, Nk, d)).copy(), dtype)
+    scale = 1.0 / np.sqrt(d)
+    o, _ = _forward(*(to_device(x, dtype) for x in (q, k, v)), form, scale)
+    want = np.broadcast_to(synth.widen(v, dtype)[0, 0, 0], (B, H, Nq, d))
+    assert_close_o(from_device(o), want, dtype, f"{form}/{dtype}/d{d} constant V")
+
+
+@pytest.mark.parametrize("form", FORMS)
+def test_zero_queries_average_v(form):
+    dtype, B, H, Nq, Nk, d = "f16", 2, 1, 64, 1000, 40
+    q = synth.round_to(np.zeros((B, H, Nq, d)), dtype)
+    k = synth.tensor(21, (B, H, Nk, d), dtype)
+    v = synth.tensor(22, (B, H, Nk, d), dtype)
+    o, ml = _forward(*(to_device(x, dtype) for x in (q, k, v)), form, 0.158)
+    vd = synth.widen(v, dtype)
+    want = np.broadcast_to(vd.mean(axis=2, keepdims=True), (B, H, Nq, d))
+    assert_close_o(from_device(o), want, dtype, f"{form} q=0")
+    mlh = from_device(ml)
+    assert np.all(mlh[..., 0] == 0.0), "m of an all-zero score row must be 0"
+    assert np.allclose(mlh[..., 1], Nk, rtol=1e-3), "l of an all-zero score row must be Nk"
+
+
+@pytest.mark.parametrize("form", FORMS)
+def test_key_shift_moves_m_only(form):
+    # values on a 1/64 grid in [-2, 2] and a shift of 0.5: every sum is exact in fp16
+    dtype, B, H, Nq, Nk, d = "f16", 1, 2, 96, 700, 40
+    grid = lambda seed, n: np.round(np.clip(synth.normal(seed, n), -2, 2) * 64) / 64
+    q = synth.round_to(grid(31, B * H * Nq * d).reshape(B, H, Nq, d), dtype)
+    k = synth.round_to(grid(32, B * H * Nk * d).reshape(B, H, Nk, d), dtype)
+    u = np.round(synth.uniform01(33, d) * 2 - 1) * 0.5
+    k2 = synth.round_to(synth.widen(k, dtype) + u, dtype)
+    assert np.array_equal(synth.widen(k2, dtype), synth.widen(k, dtype) + u)
+    v = synth.tensor(34, (B, H, Nk, d), dtype)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    dev = lambda x: to_device(x, dtype)
+    o1, ml1 = _forward(dev(q), dev(k), dev(v), form, scale)
+    o2, ml2 = _forward(dev(q), dev(k2), dev(v), form, scale)
+    o_ref, ml_ref = reference(q, k, v, dtype, scale)
+    assert_close_o(from_device(o1), o_ref, dtype, f"{form} unshifted")
+    assert_close_o(from_device(o2), o_ref, dtype, f"{form} shifted keys")
+    shift = scale * (synth.widen(q, dtype) @ u)
+    ml_ref2 = ml_ref.copy()
+    ml_ref2[..., 0] += shift
+    assert_close_ml(from_device(ml1), ml_ref, f"{form} stats unshifted")
+    assert_close_ml(from_device(ml2), ml_ref2, f"{form} stats shifted")
+
+
+@pytest.mark.parametrize("form", FORMS)
+@pytest.mark.parametrize("where", [0, 517, 4095])
+def test_dominant_key_takes_the_weight(form, where):
+    dtype, B, H, Nq, Nk, d = "f16", 1, 1, 128, 4096, 40
+    q = synth.tensor(41, (B, H, Nq, d), dtype, 0.5)
+    k = synth.tensor(42, (B, H, Nk, d), dtype, 0.5)
+    v = synth.tensor(43, (B, H, Nk, d), dtype)
+    # the chosen key is a long vector along the mean query direction: for the
+    # queries on its side it outweighs all other keys together
+    qbar = synth.widen(q, dtype)[0, 0].mean(axis=0)
+    k[0, 0, where] = synth.round_to(qbar / np.linalg.norm(qbar) * 200.0, dtype)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    o, ml = _forward(*(to_device(x, dtype) for x in (q, k, v)), form, scale)
+    o_ref, ml_ref = reference(q, k, v, dtype, scale)
+    assert_close_o(from_device(o), o_ref, dtype, f"{form} dominant key at {where}")
+    assert_close_ml(from_device(ml), ml_ref, f"{form} dominant key at {where}")
+
+
+@pytest.mark.parametrize("form", FORMS)
+@pytest.mark.parametrize("dtype,d", [("f16", 40), ("bf16", 40), ("f16", 80), ("f16", 160)])
+def test_rising_scores_rebase_every_block(form, dtype, d):
+    # key j carries +j along the queries' mean direction: for the queries on
+    # that side each 64-key block raises the row max by about 8 (in exp2
+    # units), so the online state moves on nearly every block
+    B, H, Nq, Nk = 1, 1, 160, 2100
+    q = synth.tensor(51, (B, H, Nq, d), dtype, 0.5)
+    qd = synth.widen(q, dtype)[0, 0]
+    dirn = qd.mean(axis=0)
+    dirn /= np.linalg.norm(dirn)
+    kd = synth.normal(52, Nk * d).reshape(Nk, d) * 0.3 + np.arange(Nk)[:, None] * 1.0 * dirn
+    k = synth.round_to(kd.reshape(B, H, Nk, d), dtype)
+    v = synth.tensor(53, (B, H, Nk, d), dtype)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    o, ml = _forward(*(to_device(x, dtype) for x in (q, k, v)), form, scale)
+    o_ref, ml_ref = reference(q, k, v, dtype, scale)
+    assert_close_o(from_device(o), o_ref, dtype, f"{form}/{dtype}/d{d} rising scores")
+    assert_close_ml(from_device(ml), ml_ref, f"{form}/{dtype}/d{d} rising scores")
+
+
+@pytest.mark.parametrize("form", FORMS)
+def test_peaked_softmax_large_logits(form):
+    # Q, K ~ N(0, 3^2): scores spread over hundreds, most weights underflow
+    cfg = CONFIGS["level2_self"]
+    dtype, B, H, Nq, Nk, d = "f16", 1, 2, 256, 1024, 80
+    q = synth.tensor(61, (B, H, Nq, d), dtype, 3.0)
+    k = synth.tensor(62, (B, H, Nk, d), dtype, 3.0)
+    v = synth.tensor(63, (B, H, Nk, d), dtype)
+    o, ml = _forward(*(to_device(x, dtype) for x in (q, k, v)), form, cfg.scale)
+    o_ref, ml_ref = reference(q, k, v, dtype, cfg.scale)
+    assert_close_o(from_device(o), o_ref, dtype, f"{form} large logits")
+    assert_close_ml(from_device(ml), ml_ref, f"{form} large logits")
+
+
+@pytest.mark.parametrize("name", ["sd512_cross", "level2_self"])
+def test_bitwise_repeatable_and_stream_independent(name):
+    import torch
+    import attention_attn_stats_amd as attn
+    cfg = CONFIGS[name]
+    q, k, v = (to_device(x, cfg.dtype) for x in cfg.inputs())
+    ref = {f: [t.clone() for t in _forward(q, k, v, f, cfg.scale)] for f in FORMS}
+    ref["auto"] = [attn.forward(q, k, v, scale=cfg.scale)[0].clone()]
+    for _ in range(3):
+        for f in FORMS:
+            got = _forward(q, k, v, f, cfg.scale)
+            for a, b in zip(got, ref[f]):
+                assert torch.equal(a, b), f"{name}/{f}: repeated launch differs"
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        got = {f: _forward(q, k, v, f, cfg.scale) for f in FORMS}
+        got_auto = attn.forward(q, k, v, scale=cfg.scale)[0]
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for f in FORMS:
+        for a, b in zip(got[f], ref[f]):
+            assert torch.equal(a, b), f"{name}/{f}: side-stream result differs"
+    assert torch.equal(got_auto, ref["auto"][0])
