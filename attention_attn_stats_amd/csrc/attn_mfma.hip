@@ -166,15 +166,17 @@ __device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
 }
 
 // ---------------------------------------------------------------------------
-// Forward kernel: FlashAttention (online softmax) or the PV pass of the
+// Forward kernel: FlashAttention (online softmax), or either pass of the
 // partially fused softmax.
 //
-// One workgroup = 8 waves = 4 query groups of 32 queries x 2 key halves; the
-// two waves of a query group walk alternate 32-key blocks (the key range is
-// split in two, as in the block-split reduction; 64-key blocks at d = 40,
-// 32 otherwise) and merge their partial
-// (m, l, O) through LDS at the end.  K and V blocks go through a ring of LDS
-// slots per key half, filled cooperatively by that half's waves.
+// One workgroup = QG query groups of 32 queries x 2 key halves (QG = 8, a
+// 1024-thread workgroup per CU, at d = 40; QG = 4 otherwise); the two waves of
+// a query group walk alternate key blocks (the key range is split in two, as
+// in the block-split reduction; 64-key blocks at d = 40, 32 otherwise) and
+// merge their partial (m, l, O) through LDS at the end.  K and V blocks go
+// through a ring of LDS slots per key half, filled cooperatively by that
+// half's waves; more query groups per workgroup means fewer K/V copies per
+// query from L2 into LDS.
 //
 //   * S^T = K Q^T on 32x32x16 MFMAs: a 32-key x 32-query tile per block, the
 //     head dim in K=16 steps.  Lane l owns query l % 32 and 16 of the 32 keys;
@@ -194,12 +196,7 @@ __device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
 // ds_read_b64_tr_b16 takes per half wave fall in distinct LDS banks.
 __device__ __forceinline__ int vrow(int k) { return k ^ (((k >> 4) & 1) << 2); }
 
-constexpr int kQG = 4;              // query groups per workgroup
-constexpr int kW = 2 * kQG;         // waves per workgroup (x 2 key halves)
-constexpr int kT = 64 * kW;         // threads per workgroup
-constexpr int kHT = 64 * kQG;       // threads per key half
 constexpr int kQ = 32;              // queries per wave
-constexpr int kQWG = kQG * kQ;      // queries per workgroup
 
 template <int D>
 struct Shape {
@@ -214,6 +211,11 @@ struct Shape {
   static constexpr int PK = D == 40 ? 56 : D + 8;
   static constexpr int PV = D == 40 ? 48 : (D == 80 ? 80 : D + 16);
   static constexpr int BN = D == 40 ? 64 : 32;   // keys per block
+  static constexpr int QG = D == 40 ? 8 : 4;     // query groups per workgroup
+  static constexpr int W = 2 * QG;               // waves per workgroup (x 2 key halves)
+  static constexpr int T = 64 * W;               // threads per workgroup
+  static constexpr int HT = 64 * QG;             // threads per key half
+  static constexpr int QWG = QG * kQ;            // queries per workgroup
   static constexpr int NT = BN / 32;             // 32-key score tiles per block
   static constexpr int NBUF = D >= 160 ? 2 : 3;  // ring slots per key half
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
@@ -222,7 +224,7 @@ struct Shape {
 };
 
 template <class TR, int D, int MODE>
-__global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(Shape<D>::T) void fwd_kernel(const uint16_t* __restrict__ q,
                                                  const uint16_t* __restrict__ k,
                                                  const uint16_t* __restrict__ v,
                                                  uint16_t* __restrict__ out,
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
                                                  int qtiles, int nwg, float scale) {
   using S = Shape<D>;
   constexpr int KS = S::KS, MT = S::MT, PK = S::PK, PV = S::PV, NBUF = S::NBUF;
-  constexpr int BN = S::BN, NT = S::NT;
+  constexpr int BN = S::BN, NT = S::NT, kQG = S::QG, kHT = S::HT, kQWG = S::QWG;
   // Fold scale and max subtraction into the MFMA (fp16, d with a spare dim).
   // Not when (m, l) is reported: the pre-scaled Q perturbs the scores by up to
   // a few 1e-4 of their exp2 value, too close to the 1e-3 bound on l.
@@ -622,10 +624,11 @@ __global__ __launch_bounds__(kT) void fwd_kernel(const uint16_t* __restrict__ q,
 
 template <class TR, int D, int MODE>
 hipError_t launch_fwd_t(const Problem& p) {
+  constexpr int kQWG = Shape<D>::QWG;
   const int qtiles = (p.Nq + kQWG - 1) / kQWG;
   const long long nwg = (long long)p.BH * qtiles;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_kernel<TR, D, MODE>), dim3((unsigned)nwg), dim3(kT), 0, p.stream,
+  hipLaunchKernelGGL((fwd_kernel<TR, D, MODE>), dim3((unsigned)nwg), dim3(Shape<D>::T), 0, p.stream,
                      (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v, (uint16_t*)p.out,
                      p.ml, p.Nq, p.Nk, qtiles, (int)nwg, p.scale);
   return hipGetLastError();
