@@ -14,7 +14,8 @@ sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
                     [--variant auto|pf|flash] [--no-cpu-baseline]
-                    [--configs-out FILE]   # also time every config, write JSONL there
+                    [--configs-out FILE]   # also time every config and form, JSONL there
+                    [--cold]               # configs table: evict the caches between steps
 """
 from __future__ import annotations
 
@@ -121,6 +122,84 @@ def time_config(cfg, variant: str, steps: int, warmup: int):
     return {"variant": chosen, "ms_per_step": wall * 1e3 / steps, "kernel_ms": kern}
 
 
+def algorithmic_bytes(cfg, form: str) -> dict:
+    """HBM bytes each form must move at least once (element size from dtype)."""
+    es = {"f16": 2, "bf16": 2, "f32": 4}[cfg.dtype]
+    bh = cfg.B * cfg.H
+    q, kv, ml = bh * cfg.Nq * cfg.d * es, bh * cfg.Nk * cfg.d * es, bh * cfg.Nq * 8
+    stats = q + kv + ml                     # pass 1: read Q, K; write ml
+    pv = q + 2 * kv + ml + q                # pass 2: read Q, K, V, ml; write O
+    return {"flash": q + 2 * kv + q, "pf": stats + pv, "stats": stats}
+
+
+def time_steps(cfg, form: str, steps: int, warmup: int, cold: bool):
+    """Per-step times (ms) with events around every step, for the median / min
+    of the configs table.  `cold` rewrites a 512 MiB buffer before every step
+    (outside the events) so that K and V come from HBM, not L2 / MALL."""
+    import statistics
+    import torch
+    import attention_attn_stats_amd as attn
+    q, k, v = device_inputs(cfg)
+    out = torch.empty_like(q)
+    ml = torch.empty((cfg.B, cfg.H, cfg.Nq, 2), device=q.device, dtype=torch.float32)
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=q.device) if cold else None
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(warmup + steps):
+        if scrub is not None:
+            scrub.fill_(i & 0xFF)
+        e = ev[i - warmup] if i >= warmup else None
+        if e:
+            e[0].record(stream)
+        if form == "flash":
+            attn.flash(q, k, v, out=out, scale=cfg.scale)
+            if e:
+                e[1].record(stream)
+        else:
+            attn.stats(q, k, ml=ml, scale=cfg.scale)
+            if e:
+                e[1].record(stream)
+            attn.pv(q, k, v, ml, out=out, scale=cfg.scale)
+        if e:
+            e[2].record(stream)
+    torch.cuda.synchronize()
+    step = [e[0].elapsed_time(e[2]) for e in ev]
+    first = [e[0].elapsed_time(e[1]) for e in ev]
+    return {"median_ms": statistics.median(step), "min_ms": min(step),
+            "first_kernel_median_ms": statistics.median(first)}
+
+
+def config_record(cfg, form: str, steps: int, cold: bool) -> dict:
+    """TFLOP/s, % of the MFMA peak and the roofline fraction t_roof / t of one
+    config and form (t_roof = max(FLOP / peak, bytes / 8 TB/s))."""
+    t = time_steps(cfg, form, steps, 5, cold)
+    peak = PEAK_TFLOPS[cfg.dtype]
+    by = algorithmic_bytes(cfg, form)
+    t_roof = max(cfg.flops / (peak * 1e12), by[form] / (HBM_GBS * 1e9))
+    rec = {"config": cfg.name, "variant": form, "dtype": cfg.dtype, "cold": cold,
+           "median_us": round(t["median_ms"] * 1e3, 2), "min_us": round(t["min_ms"] * 1e3, 2),
+           "tflops": round(cfg.flops / (t["median_ms"] * 1e-3) / 1e12, 2),
+           "pct_peak": round(100 * cfg.flops / (t["median_ms"] * 1e-3) / 1e12 / peak, 2),
+           "algorithmic_bytes": by[form], "t_roof_us": round(t_roof * 1e6, 3),
+           "roofline_frac": round(t_roof / (t["median_ms"] * 1e-3), 4)}
+    if form == "pf":
+        ts = t["first_kernel_median_ms"] * 1e-3
+        rec["stats_pass_us"] = round(ts * 1e6, 2)
+        rec["stats_pass_GBps"] = round(by["stats"] / ts / 1e9, 1)
+    return rec
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, budget_s: float = 12.0):
     """The float64 oracle timed on a bounded sample of the workload: whole
     heads (all Nq query rows against all Nk keys), as many passes over the
@@ -143,6 +222,7 @@ def cpu_baseline(cfg, budget_s: float = 12.0):
     t = time.perf_counter() - t0
     flops = 4.0 * done * cfg.Nq * cfg.Nk * cfg.d
     return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"{done} head evaluations ({done / bh:.1f} passes over the {bh} heads of {cfg.name}; "
                       f"each {cfg.Nq} queries x {cfg.Nk} keys x d={cfg.d}, float64, score matrix "
                       f"materialised), {t:.1f} s wall"}
@@ -157,6 +237,7 @@ def main():
     ap.add_argument("--variant", default="auto", choices=["auto", "pf", "flash"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--configs-out", default=None)
+    ap.add_argument("--cold", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times (calibrates the "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -207,16 +288,15 @@ def main():
         "pct_fp16_mfma_peak": round(100.0 * tflops / PEAK_TFLOPS["f16"], 2),
         "kernel_ms": {k_: round(v_, 5) for k_, v_ in r["kernel_ms"].items()},
         "roofline": roof,
+        # time at the binding roof (MFMA here) over the measured step time
+        "t_roof_frac": round(max(flops / (peak * 1e12), algorithmic_bytes(cfg, r["variant"])[r["variant"]]
+                                 / (HBM_GBS * 1e9)) / (r["ms_per_step"] * 1e-3), 4),
     }
     if args.configs_out:
         with open(args.configs_out, "w") as f:
             for name, c in CONFIGS.items():
                 for var in ("pf", "flash"):
-                    rr = time_config(c, var, max(20, args.steps // 4), 5)
-                    t = c.flops / (rr["ms_per_step"] * 1e-3) / 1e12
-                    rec = {"config": name, "variant": var, "dtype": c.dtype, "ms_per_step": rr["ms_per_step"],
-                           "kernel_ms": rr["kernel_ms"], "tflops": t,
-                           "pct_peak": 100 * t / PEAK_TFLOPS[c.dtype]}
+                    rec = config_record(c, var, max(20, args.steps // 4), args.cold)
                     f.write(json.dumps(rec) + "\n")
                     log(json.dumps(rec))
     if not args.no_cpu_baseline:
