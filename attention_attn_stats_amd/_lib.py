@@ -16,7 +16,8 @@ F32, F16, BF16 = 0, 1, 2
 AUTO, PARTIAL_FUSED, FLASH = 0, 1, 2
 
 EXPORTS = ("attn_stats", "attn_pv", "attn_flash", "attn_forward", "attn_select",
-           "attn_default_variant", "attn_select_reset", "attn_status_string")
+           "attn_default_variant", "attn_select_reset", "attn_status_string",
+           "attn_scores", "attn_scores_stats", "attn_scores_pv")
 
 _lib = None
 
@@ -55,6 +56,12 @@ def load() -> ctypes.CDLL:
     lib.attn_default_variant.restype = _i
     lib.attn_select_reset.argtypes = []
     lib.attn_select_reset.restype = None
+    lib.attn_scores.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]
+    lib.attn_scores.restype = _i
+    lib.attn_scores_stats.argtypes = [_vp, _vp, _i, _i, _i, _i, _vp]
+    lib.attn_scores_stats.restype = _i
+    lib.attn_scores_pv.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
+    lib.attn_scores_pv.restype = _i
     lib.attn_status_string.argtypes = [_i]
     lib.attn_status_string.restype = ctypes.c_char_p
     _lib = lib

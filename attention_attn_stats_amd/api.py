@@ -107,6 +107,57 @@ def forward(q, k, v, variant="auto", out=None, ml=None, scale=None):
     return out, ml
 
 
+def _a_for(B, H, Nq, Nk, device, a):
+    if a is None:
+        return torch.empty((B, H, Nq, Nk), device=device, dtype=torch.float32)
+    if a.shape != (B, H, Nq, Nk) or a.dtype != torch.float32 or not a.is_contiguous() or not a.is_cuda:
+        raise ValueError("a must be a contiguous float32 [B, H, Nq, Nk] device tensor")
+    return a
+
+
+def scores(q, k, a=None, scale=None):
+    """The stored logit matrix A = scale q k^T -> a [B, H, Nq, Nk] float32."""
+    B, H, Nq, Nk, d = _dims(q, k, None)
+    a = _a_for(B, H, Nq, Nk, q.device, a)
+    _check(_lib.load().attn_scores(q.data_ptr(), k.data_ptr(), a.data_ptr(), B, H, Nq, Nk, d,
+                                   _scale(scale, d), _DT[q.dtype], _stream()), "attn_scores")
+    return a
+
+
+def scores_stats(a, ml=None):
+    """Row statistics (m, l) of a stored A -> ml [B, H, Nq, 2] float32."""
+    if a.dim() != 4 or a.dtype != torch.float32 or not a.is_cuda or not a.is_contiguous():
+        raise ValueError("a must be a contiguous float32 [B, H, Nq, Nk] device tensor")
+    B, H, Nq, Nk = a.shape
+    if ml is None:
+        ml = torch.empty((B, H, Nq, 2), device=a.device, dtype=torch.float32)
+    elif ml.shape != (B, H, Nq, 2) or ml.dtype != torch.float32 or not ml.is_contiguous() or not ml.is_cuda:
+        raise ValueError("ml must be a contiguous float32 [B, H, Nq, 2] device tensor")
+    _check(_lib.load().attn_scores_stats(a.data_ptr(), ml.data_ptr(), B, H, Nq, Nk, _stream()),
+           "attn_scores_stats")
+    return ml
+
+
+def scores_pv(a, ml, v, out=None):
+    """O = softmax(A) v from a stored A and its statistics -> out [B, H, Nq, d]."""
+    if a.dim() != 4 or a.dtype != torch.float32 or not a.is_cuda or not a.is_contiguous():
+        raise ValueError("a must be a contiguous float32 [B, H, Nq, Nk] device tensor")
+    B, H, Nq, Nk = a.shape
+    if v.dim() != 4 or tuple(v.shape[:3]) != (B, H, Nk) or not v.is_cuda or not v.is_contiguous():
+        raise ValueError(f"v shape {tuple(v.shape)} does not match a {tuple(a.shape)}")
+    if v.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {v.dtype}")
+    if ml.shape != (B, H, Nq, 2) or ml.dtype != torch.float32 or not ml.is_contiguous():
+        raise ValueError("ml must be a contiguous float32 [B, H, Nq, 2] device tensor")
+    d = v.shape[3]
+    out = torch.empty((B, H, Nq, d), device=v.device, dtype=v.dtype) if out is None else out
+    if out.shape != (B, H, Nq, d) or out.dtype != v.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, H, Nq, d] tensor of v's dtype")
+    _check(_lib.load().attn_scores_pv(a.data_ptr(), ml.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, Nq, Nk,
+                                      d, _DT[v.dtype], _stream()), "attn_scores_pv")
+    return out
+
+
 def select(B, H, Nq, Nk, d, dtype=torch.float16) -> str:
     """The variant 'auto' uses for this shape ('pf' or 'flash'); may time both."""
     r = _lib.load().attn_select(B, H, Nq, Nk, d, _DT[dtype], _stream())

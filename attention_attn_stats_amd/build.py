@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libattn.so")
-SOURCES = ["attn_api.cpp", "attn_mfma.hip", "attn_f32.hip"]
+SOURCES = ["attn_api.cpp", "attn_mfma.hip", "attn_f32.hip", "attn_scores.hip"]
 ARCH = os.environ.get("ATTN_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
@@ -60,21 +60,27 @@ def unverified_mfma(asm_text: str) -> list:
     return bad
 
 
+MFMA_SOURCES = ["attn_mfma.hip", "attn_scores.hip"]
+
+
 def verify_device_code(hipcc: str, verbose: bool = False, defines=()) -> None:
-    """Compile the matrix-core source to gfx950 assembly and reject unverified MFMA opcodes."""
-    with tempfile.TemporaryDirectory() as td:
-        asm = os.path.join(td, "attn_mfma.s")
-        cmd = [hipcc, *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-x", "hip", "--cuda-device-only", "-S",
-               os.path.join(CSRC, "attn_mfma.hip"), "-o", asm]
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            raise RuntimeError("device assembly generation failed:\n" + r.stderr)
-        text = open(asm).read()
-    bad = unverified_mfma(text)
-    if bad:
-        raise RuntimeError("unverified MFMA opcodes in device code:\n" + "\n".join(bad[:10]))
+    """Compile the matrix-core sources to gfx950 assembly and reject unverified MFMA opcodes."""
+    total = 0
+    for src in MFMA_SOURCES:
+        with tempfile.TemporaryDirectory() as td:
+            asm = os.path.join(td, src + ".s")
+            cmd = [hipcc, *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-x", "hip", "--cuda-device-only", "-S",
+                   os.path.join(CSRC, src), "-o", asm]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"device assembly generation failed for {src}:\n" + r.stderr)
+            text = open(asm).read()
+        bad = unverified_mfma(text)
+        if bad:
+            raise RuntimeError(f"unverified MFMA opcodes in {src}:\n" + "\n".join(bad[:10]))
+        total += text.count("v_mfma_")
     if verbose:
-        print(f"verified {text.count('v_mfma_')} MFMA instructions are all of {sorted(VERIFIED_MFMA)}")
+        print(f"verified {total} MFMA instructions are all of {sorted(VERIFIED_MFMA)}")
 
 
 def build(verbose: bool = False, out: str = LIB, defines=()) -> str:

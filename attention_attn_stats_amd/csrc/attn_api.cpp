@@ -46,6 +46,7 @@ Problem make(const void* q, const void* k, const void* v, void* out, float* ml, 
   p.v = v;
   p.out = out;
   p.ml = ml;
+  p.a = nullptr;
   p.BH = B * H;
   p.Nq = Nq;
   p.Nk = Nk;
@@ -220,6 +221,48 @@ attn_status attn_forward(const void* q, const void* k, const void* v, void* out,
     return run_flash(pf);
   }
   return run_pf(p);
+}
+
+// ---- the partially fused form over a stored logit matrix ------------------
+namespace {
+// A = [B][H][Nq][Nk] float32: a head's part must stay below 2^31 bytes (the
+// kernels address it with 32-bit offsets), the whole within size_t.
+attn_status check_scores(int B, int H, int Nq, int Nk) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return ATTN_ERR_INVALID_ARG;
+  if ((long long)Nq * Nk * 4 >= 0x7fffffffLL) return ATTN_ERR_INVALID_ARG;
+  if ((long long)B * H * Nq >= 0x7fffffffLL) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+}  // namespace
+
+attn_status attn_scores(const void* q, const void* k, float* a, int B, int H, int Nq, int Nk, int d,
+                        float scale, attn_dtype dt, void* stream) {
+  if (!q || !k || !a || !aligned16(q) || !aligned16(k) || ((uintptr_t)a & 3u)) return ATTN_ERR_INVALID_ARG;
+  attn_status s = check_common(B, H, Nq, Nk, d, scale, dt);
+  if (s == ATTN_OK) s = check_scores(B, H, Nq, Nk);
+  if (s != ATTN_OK) return s;
+  if (dt == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  return to_status(attn::launch_scores(make(q, k, nullptr, nullptr, nullptr, B, H, Nq, Nk, d, scale, dt, stream), a));
+}
+
+attn_status attn_scores_stats(const float* a, float* ml, int B, int H, int Nq, int Nk, void* stream) {
+  if (!a || !ml || ((uintptr_t)a & 3u) || ((uintptr_t)ml & 7u)) return ATTN_ERR_INVALID_ARG;
+  attn_status s = check_scores(B, H, Nq, Nk);
+  if (s != ATTN_OK) return s;
+  return to_status(attn::launch_scores_stats(a, ml, (long long)B * H * Nq, Nk, (hipStream_t)stream));
+}
+
+attn_status attn_scores_pv(const float* a, const float* ml, const void* v, void* out, int B, int H, int Nq,
+                           int Nk, int d, attn_dtype dt, void* stream) {
+  if (!a || !ml || !v || !out || ((uintptr_t)a & 3u) || ((uintptr_t)ml & 7u) || !aligned16(v) || !aligned16(out))
+    return ATTN_ERR_INVALID_ARG;
+  attn_status s = check_common(B, H, Nq, Nk, d, 1.f, dt);
+  if (s == ATTN_OK) s = check_scores(B, H, Nq, Nk);
+  if (s != ATTN_OK) return s;
+  if (dt == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  Problem p = make(nullptr, nullptr, v, out, const_cast<float*>(ml), B, H, Nq, Nk, d, 1.f, dt, stream);
+  p.a = a;
+  return to_status(attn::launch_mfma_pv_scores(p));
 }
 
 attn_variant attn_select(int B, int H, int Nq, int Nk, int d, attn_dtype dt, void* stream) {

@@ -81,6 +81,7 @@ constexpr int kModeFlash = 0;    // online softmax, O only
 constexpr int kModeFlashML = 1;  // online softmax, O and (m, l)
 constexpr int kModePV = 2;       // softmax from given (m, l), O only
 constexpr int kModeStats = 3;    // (m, l) only: the first pass of the partially fused form
+constexpr int kModePVScores = 4; // as kModePV, the logits read from a stored A instead of Q K^T
 
 // max of two pairs of non-negative fp16 values (v_pk_maximum3_f16 from chains)
 __device__ __forceinline__ uint32_t pmax(uint32_t a, uint32_t b) {
@@ -127,23 +128,6 @@ __device__ __forceinline__ int xcd_tile(int nwg) {
 // treats the two results of the swap builtins as interchangeable in that case
 // and folds a reduction over them away.  The leading s_nop covers the wait
 // states a swap needs after a vector-ALU write of its inputs.
-template <class Op>
-__device__ __forceinline__ float group_reduce(float x, Op op) {
-  // over the four 16-lane groups (lanes li, li+16, li+32, li+48)
-  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
-  asm volatile("s_nop 4\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-  x = op(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
-  a = __builtin_bit_cast(uint32_t, x);
-  b = a;
-  asm volatile("s_nop 4\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-  return op(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
-}
-__device__ __forceinline__ float group_max(float x) {
-  return group_reduce(x, [](float a, float b) { return __builtin_fmaxf(a, b); });
-}
-__device__ __forceinline__ float group_sum(float x) {
-  return group_reduce(x, [](float a, float b) { return a + b; });
-}
 // over lanes l and l ^ 32
 template <class Op>
 __device__ __forceinline__ float pair_reduce(float x, Op op) {
@@ -228,8 +212,8 @@ __global__ __launch_bounds__(Shape<D>::T) void fwd_kernel(const uint16_t* __rest
                                                  const uint16_t* __restrict__ k,
                                                  const uint16_t* __restrict__ v,
                                                  uint16_t* __restrict__ out,
-                                                 float* __restrict__ ml, int Nq, int Nk,
-                                                 int qtiles, int nwg, float scale) {
+                                                 float* __restrict__ ml, const float* __restrict__ a,
+                                                 int Nq, int Nk, int qtiles, int nwg, float scale) {
   using S = Shape<D>;
   constexpr int KS = S::KS, MT = S::MT, PK = S::PK, PV = S::PV, NBUF = S::NBUF;
   constexpr int BN = S::BN, NT = S::NT, kQG = S::QG, kHT = S::HT, kQWG = S::QWG;
@@ -237,10 +221,12 @@ __global__ __launch_bounds__(Shape<D>::T) void fwd_kernel(const uint16_t* __rest
   // Not when (m, l) is reported: the pre-scaled Q perturbs the scores by up to
   // a few 1e-4 of their exp2 value, too close to the 1e-3 bound on l.
   constexpr bool kStats = MODE == kModeStats;
+  constexpr bool kFromA = MODE == kModePVScores;             // logits read from A (float32)
+  constexpr bool kPVLike = MODE == kModePV || kFromA;        // (m, l) given, O only
   constexpr bool kReportML = MODE == kModeFlashML || kStats;
   // where l comes from: the matrix cores (V's ones column in the flash forms,
   // a ones operand in the stats form) or fp32 sums on the vector ALU
-  constexpr bool kValuSum = MODE != kModePV && (kStats ? !TR::kRoundedSumOk
+  constexpr bool kValuSum = !kPVLike && (kStats ? !TR::kRoundedSumOk
                                                        : (!S::kOnes || (kReportML && !TR::kRoundedSumOk)));
   constexpr int MO = kStats ? 1 : MT;  // 16-row tiles of the accumulator (stats: the row sums)
   // floats per lane handed from one key half to the other in the merge: O
@@ -258,7 +244,8 @@ __global__ __launch_bounds__(Shape<D>::T) void fwd_kernel(const uint16_t* __rest
   const int qg = wave % kQG, half = wave / kQG, htid = tid % kHT;
   const int l32 = lane & 31, hi = lane >> 5;  // 32x32 layout: query l32, key subgroup hi
   const int G = lane >> 4, li = lane & 15;    // 16x16 layout
-  const float c = scale * kLog2e;
+  // exp2 units: the stored A already carries the scale
+  const float c = kFromA ? kLog2e : scale * kLog2e;
 
   const int tile = xcd_tile(nwg);
   const int head = tile / qtiles;
@@ -285,7 +272,7 @@ __global__ __launch_bounds__(Shape<D>::T) void fwd_kernel(const uint16_t* __rest
   // (in fp32) from every score.  The online form starts from 0 and always
   // re-bases on its first block.
   float mref = 0.f;
-  if constexpr (MODE == kModePV) {
+  if constexpr (kPVLike) {
     const int row = qbase + l32;
     mref = row < Nq ? ml[((size_t)head * Nq + row) * 2] * kLog2e : 0.f;  // stored in natural units
   }
@@ -294,7 +281,10 @@ __global__ __launch_bounds__(Shape<D>::T) void fwd_kernel(const uint16_t* __rest
   // to 16 bits would move a score by up to 2^-11 of its own size, which is
   // visible in P once scores reach tens.
   s8v qf[KS];
-  {
+  if constexpr (kFromA) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = (s8v){0, 0, 0, 0, 0, 0, 0, 0};  // Q is not read
+  } else {
     const int row = qbase + l32;
     const bool ok = row < Nq;
     const uint16_t* qp = qh + (size_t)(ok ? row : 0) * D;
@@ -323,9 +313,15 @@ __global__ __launch_bounds__(Shape<D>::T) void fwd_kernel(const uint16_t* __rest
   // buffer resource starts at the block's first key and ends at key Nk, so
   // the block address is scalar work and rows past Nk come back as zeros.
   constexpr int VCH = PV / 8;                                 // chunks per V row (incl. padding)
-  constexpr int KJOBS = BN * S::CPR / 64, NJOB = KJOBS + (kStats ? 0 : (BN * VCH + 63) / 64);
+  // (reading A, the K blocks are not needed)
+  constexpr int KJOBS = kFromA ? 0 : BN * S::CPR / 64, NJOB = KJOBS + (kStats ? 0 : (BN * VCH + 63) / 64);
   constexpr int JPW = (NJOB + kQG - 1) / kQG;                 // jobs per wave
   static_assert(BN * S::CPR % 64 == 0, "K staging covers whole waves");
+  // A rows of this head (float32 [Nq][Nk]): lane l32 reads row qbase + l32
+  // (rows past Nq are past the resource and read as zero)
+  const __amdgpu_buffer_rsrc_t ars =
+      make_rsrc(kFromA ? (const void*)(a + (size_t)head * Nq * Nk) : (const void*)kh, kFromA ? Nq * Nk * 4 : 0);
+  const int arow = (qbase + l32) * Nk;
   const int halfu = __builtin_amdgcn_readfirstlane(half);
   const int qgu = __builtin_amdgcn_readfirstlane(qg);
   int goff[JPW], soff[JPW];  // byte offset in the block (< 0: no chunk), element offset in the slot
@@ -449,12 +445,22 @@ __global__ __launch_bounds__(Shape<D>::T) void fwd_kernel(const uint16_t* __rest
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         x[t] = (f16v){};
+        if constexpr (kFromA) {
+          // the same 32x32 layout, from memory: keys (i/4)*8 + hi*4 + (i%4) of the tile
+          const int k0 = kb * BN + t * 32 + hi * 4;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int d0 = ks * 16 + hi * 8;
-          // past d the LDS padding is zero (and so is Q)
-          const s8v a = *(const s8v*)(Ks + (t * 32 + l32) * PK + d0);
-          x[t] = TR::mma32(a, qf[ks], x[t]);
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              x[t][4 * g + j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ars, (arow + k0 + g * 8 + j) * 4, 0, 0));
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const int d0 = ks * 16 + hi * 8;
+            // past d the LDS padding is zero (and so is Q)
+            const s8v a = *(const s8v*)(Ks + (t * 32 + l32) * PK + d0);
+            x[t] = TR::mma32(a, qf[ks], x[t]);
+          }
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) x[t][i] = __builtin_fmaf(x[t][i], c, -mref);
@@ -483,7 +489,7 @@ __global__ __launch_bounds__(Shape<D>::T) void fwd_kernel(const uint16_t* __rest
           ls = expand(x);
         }
       } else {
-        if constexpr (MODE != kModePV) {
+        if constexpr (!kPVLike) {
           const float bm = block_max(x);
           if (__any(bm > 8.f) || it == 0) rebase(x, bm);
           else mtrue = __builtin_fmaxf(mtrue, bm + mref);
@@ -534,7 +540,7 @@ __global__ __launch_bounds__(Shape<D>::T) void fwd_kernel(const uint16_t* __rest
   for (int qt = 0; qt < 2; ++qt) {
     mo[qt] = __shfl(mref, qt * 16 + li);
     mto[qt] = __shfl(mtrue, qt * 16 + li);
-    if constexpr (MODE == kModePV) {
+    if constexpr (kPVLike) {
       lo[qt] = 0.f;
       lro[qt] = 0.f;
     } else {
@@ -574,7 +580,7 @@ __global__ __launch_bounds__(Shape<D>::T) void fwd_kernel(const uint16_t* __rest
     const float lB = ex[(XO + qt * 4 + 2) * 64];
     const float lrB = ex[(XO + qt * 4 + 3) * 64];
     float fA = 1.f, fB = 1.f, M = mo[qt];
-    if constexpr (MODE != kModePV) {
+    if constexpr (!kPVLike) {
       // a half that saw no key holds (-inf, 0, 0) and contributes nothing
       M = __builtin_fmaxf(mo[qt], mB);
       fA = __builtin_amdgcn_exp2f(mo[qt] - M);
@@ -590,7 +596,7 @@ __global__ __launch_bounds__(Shape<D>::T) void fwd_kernel(const uint16_t* __rest
     const int row = qbase + qt * 16 + li;
     float inv = 0.f;
     if (row < Nq) {
-      if constexpr (MODE == kModePV) {
+      if constexpr (kPVLike) {
         // P was formed against mref = the given m (M here); the given l is
         // relative to it
         const float2 st = *(const float2*)(ml + ((size_t)head * Nq + row) * 2);
@@ -630,7 +636,7 @@ hipError_t launch_fwd_t(const Problem& p) {
   if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((fwd_kernel<TR, D, MODE>), dim3((unsigned)nwg), dim3(Shape<D>::T), 0, p.stream,
                      (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v, (uint16_t*)p.out,
-                     p.ml, p.Nq, p.Nk, qtiles, (int)nwg, p.scale);
+                     p.ml, p.a, p.Nq, p.Nk, qtiles, (int)nwg, p.scale);
   return hipGetLastError();
 }
 
@@ -650,6 +656,7 @@ hipError_t by_type(const Problem& p) {
 
 template <class TR, int D> struct StatsL { static hipError_t run(const Problem& p) { return launch_fwd_t<TR, D, kModeStats>(p); } };
 template <class TR, int D> struct PvL { static hipError_t run(const Problem& p) { return launch_fwd_t<TR, D, kModePV>(p); } };
+template <class TR, int D> struct PvAL { static hipError_t run(const Problem& p) { return launch_fwd_t<TR, D, kModePVScores>(p); } };
 template <class TR, int D> struct FlashL {
   static hipError_t run(const Problem& p) {
     return p.ml ? launch_fwd_t<TR, D, kModeFlashML>(p) : launch_fwd_t<TR, D, kModeFlash>(p);
@@ -660,6 +667,7 @@ template <class TR, int D> struct FlashL {
 
 hipError_t launch_mfma_stats(const Problem& p) { return by_type<StatsL>(p); }
 hipError_t launch_mfma_pv(const Problem& p) { return by_type<PvL>(p); }
+hipError_t launch_mfma_pv_scores(const Problem& p) { return by_type<PvAL>(p); }
 hipError_t launch_mfma_flash(const Problem& p) { return by_type<FlashL>(p); }
 
 }  // namespace attn

@@ -113,6 +113,34 @@ attn_status attn_forward(const void* q, const void* k, const void* v, void* out,
                          int B, int H, int Nq, int Nk, int d, float scale, attn_variant var,
                          attn_dtype dt, void* stream);
 
+/* ---- The partially fused softmax over a stored logit matrix ------------
+ * The same two passes with A = scale * Q K^T written to memory first, as the
+ * write-up draws the data flow (A is the input of the statistics pass and of
+ * the softmax-times-V pass).  The fused entry points above recompute A on
+ * chip instead; these three exist to run the pages' literal data flow and to
+ * measure what storing A costs.  Layout of A: [B][H][Nq][Nk] float32 (the
+ * accumulator type: 16-bit logits would move exp(a - m) by up to 2^-11 |a|).
+ * Limits in addition to the ones above: Nq * Nk * 4 < 2^31 (one head's A),
+ * a 4-byte aligned; F16 and BF16 only (F32 returns ATTN_ERR_UNSUPPORTED). */
+
+/* A = scale * Q K^T for every head.  q: [B][H][Nq][d], k: [B][H][Nk][d] (dt);
+ * a: [B][H][Nq][Nk] float32, written. */
+attn_status attn_scores(const void* q, const void* k, float* a, int B, int H, int Nq, int Nk, int d,
+                        float scale, attn_dtype dt, void* stream);
+
+/* The block-split reduction of every row of a stored A to (m, l), one launch
+ * (write-up, attention section): each row is cut into 16-byte blocks, every
+ * block reduced to its own (max, sum of exp) pair, the pairs merged with the
+ * rule given for attn_stats.  a: [B][H][Nq][Nk] float32 (read only);
+ * ml: [B][H][Nq][2] float32, written. */
+attn_status attn_scores_stats(const float* a, float* ml, int B, int H, int Nq, int Nk, void* stream);
+
+/* O = softmax(A) V from a stored A and its statistics, exponentials,
+ * normalisation and the product with V fused in one launch.  a, ml as above
+ * (read only); v: [B][H][Nk][d], out: [B][H][Nq][d] (dt), written. */
+attn_status attn_scores_pv(const float* a, const float* ml, const void* v, void* out, int B, int H, int Nq,
+                           int Nk, int d, attn_dtype dt, void* stream);
+
 /* The variant ATTN_AUTO uses for this shape.  On a cache miss it allocates
  * temporary device buffers, times both variants on `stream`, frees the
  * buffers and caches the winner, so it synchronises and may allocate; call it

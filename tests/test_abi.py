@@ -91,3 +91,24 @@ def test_pv_flash_forward_validation(lib):
         _lib.ERR_INVALID_ARG
     assert lib.attn_forward(P, P, P, P, P, 1, 1, 8, 8, 40, 0.1, 9, f, None) == _lib.ERR_UNSUPPORTED
     assert lib.attn_select(0, 1, 8, 8, 40, f, None) == _lib.AUTO
+
+
+def test_scores_entry_points_validation(lib):
+    f = _lib.F16
+    # attn_scores: pointers, alignment, sizes, element type
+    assert lib.attn_scores(None, P, P, 1, 1, 8, 8, 40, 0.1, f, None) == _lib.ERR_INVALID_ARG
+    assert lib.attn_scores(P, P, P + 2, 1, 1, 8, 8, 40, 0.1, f, None) == _lib.ERR_INVALID_ARG
+    assert lib.attn_scores(P, P, P, 1, 1, 8, 8, 64, 0.1, f, None) == _lib.ERR_UNSUPPORTED
+    assert lib.attn_scores(P, P, P, 1, 1, 8, 8, 40, 0.1, _lib.F32, None) == _lib.ERR_UNSUPPORTED
+    assert lib.attn_scores(P, P, P, 1, 1, 8, 8, 40, float("nan"), f, None) == _lib.ERR_INVALID_ARG
+    # one head's A must stay below 2^31 bytes
+    assert lib.attn_scores(P, P, P, 1, 1, 1 << 15, 1 << 14, 40, 0.1, f, None) == _lib.ERR_INVALID_ARG
+    # attn_scores_stats
+    assert lib.attn_scores_stats(None, P, 1, 1, 8, 8, None) == _lib.ERR_INVALID_ARG
+    assert lib.attn_scores_stats(P, P + 4, 1, 1, 8, 8, None) == _lib.ERR_INVALID_ARG
+    assert lib.attn_scores_stats(P, P, 1, 1, 8, 0, None) == _lib.ERR_INVALID_ARG
+    # attn_scores_pv
+    assert lib.attn_scores_pv(P, P, None, P, 1, 1, 8, 8, 40, f, None) == _lib.ERR_INVALID_ARG
+    assert lib.attn_scores_pv(P, P, P, P + 8, 1, 1, 8, 8, 40, f, None) == _lib.ERR_INVALID_ARG
+    assert lib.attn_scores_pv(P, P, P, P, 1, 1, 8, 8, 80, _lib.F32, None) == _lib.ERR_UNSUPPORTED
+    assert lib.attn_scores_pv(P, P, P, P, 1, 1, 8, 8, 48, f, None) == _lib.ERR_UNSUPPORTED
