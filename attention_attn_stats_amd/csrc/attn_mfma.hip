@@ -448,11 +448,20 @@ __global__ __launch_bounds__(Shape<D>::T) void fwd_kernel(const uint16_t* __rest
         if constexpr (kFromA) {
           // the same 32x32 layout, from memory: keys (i/4)*8 + hi*4 + (i%4) of the tile
           const int k0 = kb * BN + t * 32 + hi * 4;
+          if ((Nk & 3) == 0) {  // rows start 16-byte aligned: 4 keys per load
 #pragma unroll
-          for (int g = 0; g < 4; ++g)
+            for (int g = 0; g < 4; ++g) {
+              const f4v y = __builtin_bit_cast(f4v, __builtin_amdgcn_raw_buffer_load_b128(ars, (arow + k0 + g * 8) * 4, 0, 0));
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              x[t][4 * g + j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ars, (arow + k0 + g * 8 + j) * 4, 0, 0));
+              for (int j = 0; j < 4; ++j) x[t][4 * g + j] = y[j];
+            }
+          } else {
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                x[t][4 * g + j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ars, (arow + k0 + g * 8 + j) * 4, 0, 0));
+          }
         } else {
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {

@@ -23,6 +23,7 @@ typedef float f16v __attribute__((ext_vector_type(16)));
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef __bf16 b8v __attribute__((ext_vector_type(8)));
 typedef int i4v __attribute__((ext_vector_type(4)));
+typedef float f4v __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -105,9 +106,10 @@ __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict_
 
 // ---------------------------------------------------------------------------
 // Row statistics of A: (m_i, l_i) for every row, the block-split reduction.
-// One wave per row.  The row is cut into 16-byte blocks dealt to the lanes
-// round robin; a lane reduces its blocks to a running (max, sum of exp) pair
-// and the 64 partial pairs are merged with (m,l)+(m',l') = (M, l e^(m-M) +
+// One wave per row.  The row is cut into blocks of 4 x 16 bytes, one per lane
+// and sweep (the 16-byte pieces dealt round robin); a lane reduces each block
+// to its (max, sum of exp) pair and merges it into its running pair, and the
+// 64 partial pairs are merged with (m,l)+(m',l') = (M, l e^(m-M) +
 // l' e^(m'-M)) across the wave -- one launch, nothing but ml written.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void merge(float& m, float& l, float m2, float l2) {
@@ -119,10 +121,13 @@ __device__ __forceinline__ void merge(float& m, float& l, float m2, float l2) {
   m = M;
 }
 
+template <bool kVec>  // rows start 16-byte aligned (Nk % 4 == 0): one 16-byte load per block
 __global__ __launch_bounds__(256) void rowstats_kernel(const float* __restrict__ a, float* __restrict__ ml,
                                                        long long rows, int Nk) {
   const int lane = threadIdx.x & 63;
-  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // wave-uniform (and known so to the compiler): the buffer resource of the
+  // row lives in scalar registers
+  const long long row = (long long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= rows) return;
   const __amdgpu_buffer_rsrc_t ar = make_rsrc(a + (size_t)row * Nk, (uint32_t)Nk * 4);
   float m = -INFINITY, l = 0.f;  // in exp2 units
@@ -130,25 +135,34 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const float* __restrict__
   for (int c0 = lane * 4; c0 < Nk; c0 += 256 * U) {
     float x[U][4];
 #pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if constexpr (kVec) {
+        // cast the whole vector: a per-element bit cast of this builtin's
+        // result has been compiled into a single-dword load here
+        const f4v y = __builtin_bit_cast(f4v, __builtin_amdgcn_raw_buffer_load_b128(ar, (c0 + 256 * u) * 4, 0, 0));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[u][j] = y[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          x[u][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ar, (c0 + 256 * u + j) * 4, 0, 0));
+      }
+    }
+    // this lane's block: its U x 4 elements of this sweep (past Nk: -inf)
+    float bm = -INFINITY;
+#pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        x[u][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ar, (c0 + 256 * u + j) * 4, 0, 0));
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + 256 * u;
-      if (c >= Nk) break;
-      float bm = -INFINITY;
-#pragma unroll
       for (int j = 0; j < 4; ++j) {
-        x[u][j] = c + j < Nk ? x[u][j] * kLog2e : -INFINITY;
+        x[u][j] = c0 + 256 * u + j < Nk ? x[u][j] * kLog2e : -INFINITY;
         bm = __builtin_fmaxf(bm, x[u][j]);
       }
-      float bl = 0.f;
+    float bl = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int j = 0; j < 4; ++j) bl += __builtin_amdgcn_exp2f(x[u][j] - bm);
-      merge(m, l, bm, bl);
-    }
+    merge(m, l, bm, bl);
   }
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) {
@@ -187,7 +201,10 @@ hipError_t launch_scores(const Problem& p, float* a) {
 hipError_t launch_scores_stats(const float* a, float* ml, long long rows, int Nk, hipStream_t stream) {
   const long long nwg = (rows + 3) / 4;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(rowstats_kernel, dim3((unsigned)nwg), dim3(256), 0, stream, a, ml, rows, Nk);
+  if ((Nk & 3) == 0)
+    hipLaunchKernelGGL(rowstats_kernel<true>, dim3((unsigned)nwg), dim3(256), 0, stream, a, ml, rows, Nk);
+  else
+    hipLaunchKernelGGL(rowstats_kernel<false>, dim3((unsigned)nwg), dim3(256), 0, stream, a, ml, rows, Nk);
   return hipGetLastError();
 }
 

@@ -129,7 +129,10 @@ def algorithmic_bytes(cfg, form: str) -> dict:
     q, kv, ml = bh * cfg.Nq * cfg.d * es, bh * cfg.Nk * cfg.d * es, bh * cfg.Nq * 8
     stats = q + kv + ml                     # pass 1: read Q, K; write ml
     pv = q + 2 * kv + ml + q                # pass 2: read Q, K, V, ml; write O
-    return {"flash": q + 2 * kv + q, "pf": stats + pv, "stats": stats}
+    a = bh * cfg.Nq * cfg.Nk * 4            # the stored logit matrix (float32)
+    sc = {"scores": q + kv + a, "scores_stats": a + ml, "scores_pv": a + ml + kv + q}
+    return {"flash": q + 2 * kv + q, "pf": stats + pv, "stats": stats,
+            "pf_scores": sum(sc.values()), **sc}
 
 
 def time_steps(cfg, form: str, steps: int, warmup: int, cold: bool):
@@ -142,9 +145,11 @@ def time_steps(cfg, form: str, steps: int, warmup: int, cold: bool):
     q, k, v = device_inputs(cfg)
     out = torch.empty_like(q)
     ml = torch.empty((cfg.B, cfg.H, cfg.Nq, 2), device=q.device, dtype=torch.float32)
+    a = (torch.empty((cfg.B, cfg.H, cfg.Nq, cfg.Nk), device=q.device, dtype=torch.float32)
+         if form == "pf_scores" else None)
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device=q.device) if cold else None
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for i in range(warmup + steps):
         if scrub is not None:
             scrub.fill_(i & 0xFF)
@@ -155,6 +160,14 @@ def time_steps(cfg, form: str, steps: int, warmup: int, cold: bool):
             attn.flash(q, k, v, out=out, scale=cfg.scale)
             if e:
                 e[1].record(stream)
+        elif form == "pf_scores":
+            attn.scores(q, k, a, scale=cfg.scale)
+            if e:
+                e[1].record(stream)
+            attn.scores_stats(a, ml)
+            if e:
+                e[3].record(stream)
+            attn.scores_pv(a, ml, v, out=out)
         else:
             attn.stats(q, k, ml=ml, scale=cfg.scale)
             if e:
@@ -165,8 +178,12 @@ def time_steps(cfg, form: str, steps: int, warmup: int, cold: bool):
     torch.cuda.synchronize()
     step = [e[0].elapsed_time(e[2]) for e in ev]
     first = [e[0].elapsed_time(e[1]) for e in ev]
-    return {"median_ms": statistics.median(step), "min_ms": min(step),
-            "first_kernel_median_ms": statistics.median(first)}
+    r = {"median_ms": statistics.median(step), "min_ms": min(step),
+         "first_kernel_median_ms": statistics.median(first)}
+    if form == "pf_scores":
+        r["second_kernel_median_ms"] = statistics.median([e[1].elapsed_time(e[3]) for e in ev])
+        r["third_kernel_median_ms"] = statistics.median([e[3].elapsed_time(e[2]) for e in ev])
+    return r
 
 
 def config_record(cfg, form: str, steps: int, cold: bool) -> dict:
@@ -186,6 +203,11 @@ def config_record(cfg, form: str, steps: int, cold: bool) -> dict:
         ts = t["first_kernel_median_ms"] * 1e-3
         rec["stats_pass_us"] = round(ts * 1e6, 2)
         rec["stats_pass_GBps"] = round(by["stats"] / ts / 1e9, 1)
+    if form == "pf_scores":
+        for kname, key in (("scores", "first"), ("scores_stats", "second"), ("scores_pv", "third")):
+            tk = t[f"{key}_kernel_median_ms"] * 1e-3
+            rec[f"{kname}_us"] = round(tk * 1e6, 2)
+            rec[f"{kname}_GBps"] = round(by[kname] / tk / 1e9, 1)
     return rec
 
 
@@ -235,6 +257,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="sd512_self")
     ap.add_argument("--variant", default="auto", choices=["auto", "pf", "flash"])
+    ap.add_argument("--forms", default="pf,flash,pf_scores",
+                    help="forms timed by --configs-out (pf, flash, pf_scores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--configs-out", default=None)
     ap.add_argument("--cold", action="store_true")
@@ -295,7 +319,9 @@ def main():
     if args.configs_out:
         with open(args.configs_out, "w") as f:
             for name, c in CONFIGS.items():
-                for var in ("pf", "flash"):
+                for var in args.forms.split(","):
+                    if var == "pf_scores" and c.dtype == "f32":
+                        continue  # the stored-logit path runs on the matrix cores only
                     rec = config_record(c, var, max(20, args.steps // 4), args.cold)
                     f.write(json.dumps(rec) + "\n")
                     log(json.dumps(rec))
