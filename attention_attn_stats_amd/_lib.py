@@ -17,13 +17,27 @@ AUTO, PARTIAL_FUSED, FLASH = 0, 1, 2
 
 EXPORTS = ("attn_stats", "attn_pv", "attn_flash", "attn_forward", "attn_select",
            "attn_default_variant", "attn_select_reset", "attn_status_string",
-           "attn_scores", "attn_scores_stats", "attn_scores_pv")
+           "attn_scores", "attn_scores_stats", "attn_scores_pv",
+           "attn_stats_strided", "attn_pv_strided", "attn_flash_strided", "attn_forward_strided")
 
 _lib = None
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
 _f = ctypes.c_float
+
+
+class Strides(ctypes.Structure):
+    """attn_strides: element strides of a [B, H, N, d] tensor."""
+    _fields_ = [("batch", ctypes.c_longlong), ("head", ctypes.c_longlong), ("row", ctypes.c_longlong)]
+
+
+class Layout(ctypes.Structure):
+    """attn_layout: the strides of q, k, v and out."""
+    _fields_ = [("q", Strides), ("k", Strides), ("v", Strides), ("out", Strides)]
+
+
+_lp = ctypes.POINTER(Layout)
 
 
 class AttnError(RuntimeError):
@@ -62,6 +76,14 @@ def load() -> ctypes.CDLL:
     lib.attn_scores_stats.restype = _i
     lib.attn_scores_pv.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
     lib.attn_scores_pv.restype = _i
+    lib.attn_stats_strided.argtypes = [_vp, _vp, _vp, _lp, _i, _i, _i, _i, _i, _f, _i, _vp]
+    lib.attn_stats_strided.restype = _i
+    lib.attn_pv_strided.argtypes = [_vp, _vp, _vp, _vp, _vp, _lp, _i, _i, _i, _i, _i, _f, _i, _vp]
+    lib.attn_pv_strided.restype = _i
+    lib.attn_flash_strided.argtypes = [_vp, _vp, _vp, _vp, _vp, _lp, _i, _i, _i, _i, _i, _f, _i, _vp]
+    lib.attn_flash_strided.restype = _i
+    lib.attn_forward_strided.argtypes = [_vp, _vp, _vp, _vp, _vp, _lp, _i, _i, _i, _i, _i, _f, _i, _i, _vp]
+    lib.attn_forward_strided.restype = _i
     lib.attn_status_string.argtypes = [_i]
     lib.attn_status_string.restype = ctypes.c_char_p
     _lib = lib

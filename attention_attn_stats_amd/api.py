@@ -3,6 +3,12 @@
 Argument marshalling only: shapes and element types are checked, pointers and
 the current HIP stream are handed to libattn.so, and any non-OK status is
 raised as AttnError.  Nothing here computes attention.
+
+q, k, v and out may be strided views (for example the [B, N, H*d] activations
+of a transformer block viewed as [B, H, N, d] with
+``x.view(B, N, H, d).transpose(1, 2)``) as long as the last dimension is
+contiguous; such calls go through the *_strided entry points with the
+tensors' own strides, without a copy.
 """
 from __future__ import annotations
 
@@ -33,11 +39,40 @@ def _dims(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None):
     if v is not None and v.shape != k.shape:
         raise ValueError(f"v shape {tuple(v.shape)} must equal k shape {tuple(k.shape)}")
     for t in (q, k) + ((v,) if v is not None else ()):
-        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
-            raise ValueError("q, k, v must be contiguous device tensors of one dtype")
+        if not t.is_cuda or t.dtype != q.dtype or (t.stride(3) != 1 and t.shape[3] > 1):
+            raise ValueError("q, k, v must be device tensors of one dtype with contiguous rows")
     if q.dtype not in _DT:
         raise ValueError(f"unsupported dtype {q.dtype}")
     return B, H, Nq, k.shape[2], d
+
+
+def _strides(t: torch.Tensor) -> _lib.Strides:
+    # the stride of a dimension of extent 1 is never used; torch may report
+    # any value there, so pass one that satisfies the library's checks
+    b, h, n, d = t.shape
+    return _lib.Strides(t.stride(0) if b > 1 else 0, t.stride(1) if h > 1 else 0,
+                        t.stride(2) if n > 1 else d)
+
+
+def _layout(q, k, v=None, out=None):
+    """None when every tensor is dense (the plain entry points), else the
+    attn_layout of their strides."""
+    ts = [t for t in (q, k, v, out) if t is not None]
+    if all(t.is_contiguous() for t in ts):
+        return None
+    z = _lib.Strides(0, 0, 0)
+    return _lib.Layout(_strides(q), _strides(k), _strides(v) if v is not None else z,
+                       _strides(out) if out is not None else z)
+
+
+def _out_for(q, out):
+    if out is None:
+        return torch.empty_like(q)  # keeps q's strides when q is a dense view
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_cuda or out.stride(3) != 1:
+        raise ValueError("out must be a device tensor of q's shape and dtype with contiguous rows")
+    if torch._debug_has_internal_overlap(out) == 1:
+        raise ValueError("out must not have overlapping elements")
+    return out
 
 
 def _scale(scale, d):
@@ -65,8 +100,13 @@ def stats(q, k, ml=None, scale=None):
     """Row statistics (m, l) of A = scale q k^T -> ml [B, H, Nq, 2] float32."""
     B, H, Nq, Nk, d = _dims(q, k, None)
     ml = _ml_for(q, ml)
-    _check(_lib.load().attn_stats(q.data_ptr(), k.data_ptr(), ml.data_ptr(), B, H, Nq, Nk, d,
-                                  _scale(scale, d), _DT[q.dtype], _stream()), "attn_stats")
+    lay = _layout(q, k)
+    args = (B, H, Nq, Nk, d, _scale(scale, d), _DT[q.dtype], _stream())
+    if lay is None:
+        _check(_lib.load().attn_stats(q.data_ptr(), k.data_ptr(), ml.data_ptr(), *args), "attn_stats")
+    else:
+        _check(_lib.load().attn_stats_strided(q.data_ptr(), k.data_ptr(), ml.data_ptr(), lay, *args),
+               "attn_stats_strided")
     return ml
 
 
@@ -75,9 +115,14 @@ def pv(q, k, v, ml, out=None, scale=None):
     B, H, Nq, Nk, d = _dims(q, k, v)
     if ml.shape != (B, H, Nq, 2) or ml.dtype != torch.float32 or not ml.is_contiguous():
         raise ValueError("ml must be a contiguous float32 [B, H, Nq, 2] device tensor")
-    out = torch.empty_like(q) if out is None else out
-    _check(_lib.load().attn_pv(q.data_ptr(), k.data_ptr(), v.data_ptr(), ml.data_ptr(), out.data_ptr(),
-                               B, H, Nq, Nk, d, _scale(scale, d), _DT[q.dtype], _stream()), "attn_pv")
+    out = _out_for(q, out)
+    lay = _layout(q, k, v, out)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), ml.data_ptr(), out.data_ptr())
+    args = (B, H, Nq, Nk, d, _scale(scale, d), _DT[q.dtype], _stream())
+    if lay is None:
+        _check(_lib.load().attn_pv(*ptrs, *args), "attn_pv")
+    else:
+        _check(_lib.load().attn_pv_strided(*ptrs, lay, *args), "attn_pv_strided")
     return out
 
 
@@ -85,12 +130,16 @@ def flash(q, k, v, out=None, ml=None, want_ml=False, scale=None):
     """Single-pass online-softmax attention.  Returns out, or (out, ml) if
     want_ml or ml is given."""
     B, H, Nq, Nk, d = _dims(q, k, v)
-    out = torch.empty_like(q) if out is None else out
+    out = _out_for(q, out)
     if want_ml or ml is not None:
         ml = _ml_for(q, ml)
-    _check(_lib.load().attn_flash(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                  ml.data_ptr() if ml is not None else None, B, H, Nq, Nk, d,
-                                  _scale(scale, d), _DT[q.dtype], _stream()), "attn_flash")
+    lay = _layout(q, k, v, out)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), ml.data_ptr() if ml is not None else None)
+    args = (B, H, Nq, Nk, d, _scale(scale, d), _DT[q.dtype], _stream())
+    if lay is None:
+        _check(_lib.load().attn_flash(*ptrs, *args), "attn_flash")
+    else:
+        _check(_lib.load().attn_flash_strided(*ptrs, lay, *args), "attn_flash_strided")
     return (out, ml) if ml is not None else out
 
 
@@ -99,11 +148,15 @@ def forward(q, k, v, variant="auto", out=None, ml=None, scale=None):
     ml holds the row statistics when the partially fused form ran and is
     untouched scratch when the single pass ran (use flash(..., want_ml=True))."""
     B, H, Nq, Nk, d = _dims(q, k, v)
-    out = torch.empty_like(q) if out is None else out
+    out = _out_for(q, out)
     ml = _ml_for(q, ml)
-    _check(_lib.load().attn_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), ml.data_ptr(),
-                                    B, H, Nq, Nk, d, _scale(scale, d), _VAR[variant], _DT[q.dtype],
-                                    _stream()), "attn_forward")
+    lay = _layout(q, k, v, out)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), ml.data_ptr())
+    args = (B, H, Nq, Nk, d, _scale(scale, d), _VAR[variant], _DT[q.dtype], _stream())
+    if lay is None:
+        _check(_lib.load().attn_forward(*ptrs, *args), "attn_forward")
+    else:
+        _check(_lib.load().attn_forward_strided(*ptrs, lay, *args), "attn_forward_strided")
     return out, ml
 
 
@@ -118,6 +171,8 @@ def _a_for(B, H, Nq, Nk, device, a):
 def scores(q, k, a=None, scale=None):
     """The stored logit matrix A = scale q k^T -> a [B, H, Nq, Nk] float32."""
     B, H, Nq, Nk, d = _dims(q, k, None)
+    if not (q.is_contiguous() and k.is_contiguous()):
+        raise ValueError("scores() takes contiguous q and k")
     a = _a_for(B, H, Nq, Nk, q.device, a)
     _check(_lib.load().attn_scores(q.data_ptr(), k.data_ptr(), a.data_ptr(), B, H, Nq, Nk, d,
                                    _scale(scale, d), _DT[q.dtype], _stream()), "attn_scores")

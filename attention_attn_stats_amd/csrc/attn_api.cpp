@@ -54,6 +54,11 @@ Problem make(const void* q, const void* k, const void* v, void* out, float* ml, 
   p.scale = scale;
   p.dt = dt;
   p.stream = (hipStream_t)stream;
+  p.lay.q = attn::dense_strides(Nq, d, H);
+  p.lay.o = p.lay.q;
+  p.lay.k = attn::dense_strides(Nk, d, H);
+  p.lay.v = p.lay.k;
+  p.lay.H = H;
   return p;
 }
 
@@ -183,8 +188,50 @@ attn_status attn_flash(const void* q, const void* k, const void* v, void* out, f
   return run_flash(make(q, k, v, out, ml_out, B, H, Nq, Nk, d, scale, dt, stream));
 }
 
-attn_status attn_forward(const void* q, const void* k, const void* v, void* out, float* ml, int B, int H,
-                         int Nq, int Nk, int d, float scale, attn_variant var, attn_dtype dt, void* stream) {
+// ---- strided tensors ------------------------------------------------------
+namespace {
+// A strided [B][H][N][d] tensor: non-negative strides, rows of at least d
+// and at most 2^20 elements, every row 16-byte aligned (strides in multiples
+// of 16 bytes), the whole tensor within 2^31 elements and one head's rows
+// within 2^30 (the kernels address a head's rows, and a block of 64 rows,
+// with 32-bit byte offsets).
+attn_status check_strides(const attn_strides& s, int B, int H, int N, int d, attn_dtype dt) {
+  const long long unit = dt == ATTN_F32 ? 4 : 8;  // elements per 16 bytes
+  if (s.batch < 0 || s.head < 0 || s.row < d || s.row > (1LL << 20)) return ATTN_ERR_INVALID_ARG;
+  if (s.batch % unit || s.head % unit || s.row % unit) return ATTN_ERR_INVALID_ARG;
+  const long long head_extent = (long long)(N - 1) * s.row + d;
+  if (head_extent >= (1LL << 30)) return ATTN_ERR_INVALID_ARG;
+  if ((long long)(B - 1) * s.batch + (long long)(H - 1) * s.head + head_extent >= 0x7fffffffLL)
+    return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+attn::Strides to_internal(const attn_strides& s) {
+  attn::Strides r;
+  r.batch = s.batch;
+  r.head = s.head;
+  r.row = (int)s.row;
+  return r;
+}
+// Validates the layout of the tensors an operation uses (v, out optional) and
+// installs it in p.
+attn_status apply_layout(Problem& p, const attn_layout* lay, int B, int H, bool has_v, bool has_out) {
+  if (!lay) return ATTN_OK;  // dense
+  attn_status s = check_strides(lay->q, B, H, p.Nq, p.d, p.dt);
+  if (s == ATTN_OK) s = check_strides(lay->k, B, H, p.Nk, p.d, p.dt);
+  if (s == ATTN_OK && has_v) s = check_strides(lay->v, B, H, p.Nk, p.d, p.dt);
+  if (s == ATTN_OK && has_out) s = check_strides(lay->out, B, H, p.Nq, p.d, p.dt);
+  if (s != ATTN_OK) return s;
+  p.lay.q = to_internal(lay->q);
+  p.lay.k = to_internal(lay->k);
+  if (has_v) p.lay.v = to_internal(lay->v);
+  if (has_out) p.lay.o = to_internal(lay->out);
+  return ATTN_OK;
+}
+}  // namespace
+
+attn_status attn_forward_strided(const void* q, const void* k, const void* v, void* out, float* ml,
+                                 const attn_layout* lay, int B, int H, int Nq, int Nk, int d, float scale,
+                                 attn_variant var, attn_dtype dt, void* stream) {
   if (!q || !k || !v || !out) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || ((uintptr_t)ml & 7u))
     return ATTN_ERR_INVALID_ARG;
@@ -192,7 +239,9 @@ attn_status attn_forward(const void* q, const void* k, const void* v, void* out,
   attn_status s = check_common(B, H, Nq, Nk, d, scale, dt);
   if (s != ATTN_OK) return s;
   if (var == ATTN_PARTIAL_FUSED && !ml) return ATTN_ERR_INVALID_ARG;
-  const Problem p = make(q, k, v, out, ml, B, H, Nq, Nk, d, scale, dt, stream);
+  Problem p = make(q, k, v, out, ml, B, H, Nq, Nk, d, scale, dt, stream);
+  s = apply_layout(p, lay, B, H, true, true);
+  if (s != ATTN_OK) return s;
   if (var == ATTN_AUTO) {
     const attn_variant forced = env_override();
     if (forced != ATTN_AUTO) var = forced;
@@ -221,6 +270,11 @@ attn_status attn_forward(const void* q, const void* k, const void* v, void* out,
     return run_flash(pf);
   }
   return run_pf(p);
+}
+
+attn_status attn_forward(const void* q, const void* k, const void* v, void* out, float* ml, int B, int H,
+                         int Nq, int Nk, int d, float scale, attn_variant var, attn_dtype dt, void* stream) {
+  return attn_forward_strided(q, k, v, out, ml, nullptr, B, H, Nq, Nk, d, scale, var, dt, stream);
 }
 
 // ---- the partially fused form over a stored logit matrix ------------------
@@ -263,6 +317,43 @@ attn_status attn_scores_pv(const float* a, const float* ml, const void* v, void*
   Problem p = make(nullptr, nullptr, v, out, const_cast<float*>(ml), B, H, Nq, Nk, d, 1.f, dt, stream);
   p.a = a;
   return to_status(attn::launch_mfma_pv_scores(p));
+}
+
+
+attn_status attn_stats_strided(const void* q, const void* k, float* ml, const attn_layout* lay, int B, int H,
+                               int Nq, int Nk, int d, float scale, attn_dtype dt, void* stream) {
+  if (!q || !k || !ml || !aligned16(q) || !aligned16(k) || ((uintptr_t)ml & 7u)) return ATTN_ERR_INVALID_ARG;
+  attn_status s = check_common(B, H, Nq, Nk, d, scale, dt);
+  if (s != ATTN_OK) return s;
+  Problem p = make(q, k, nullptr, nullptr, ml, B, H, Nq, Nk, d, scale, dt, stream);
+  s = apply_layout(p, lay, B, H, false, false);
+  return s != ATTN_OK ? s : run_stats(p);
+}
+
+attn_status attn_pv_strided(const void* q, const void* k, const void* v, const float* ml, void* out,
+                            const attn_layout* lay, int B, int H, int Nq, int Nk, int d, float scale,
+                            attn_dtype dt, void* stream) {
+  if (!q || !k || !v || !ml || !out) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || ((uintptr_t)ml & 7u))
+    return ATTN_ERR_INVALID_ARG;
+  attn_status s = check_common(B, H, Nq, Nk, d, scale, dt);
+  if (s != ATTN_OK) return s;
+  Problem p = make(q, k, v, out, const_cast<float*>(ml), B, H, Nq, Nk, d, scale, dt, stream);
+  s = apply_layout(p, lay, B, H, true, true);
+  return s != ATTN_OK ? s : run_pv(p);
+}
+
+attn_status attn_flash_strided(const void* q, const void* k, const void* v, void* out, float* ml_out,
+                               const attn_layout* lay, int B, int H, int Nq, int Nk, int d, float scale,
+                               attn_dtype dt, void* stream) {
+  if (!q || !k || !v || !out) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || ((uintptr_t)ml_out & 7u))
+    return ATTN_ERR_INVALID_ARG;
+  attn_status s = check_common(B, H, Nq, Nk, d, scale, dt);
+  if (s != ATTN_OK) return s;
+  Problem p = make(q, k, v, out, ml_out, B, H, Nq, Nk, d, scale, dt, stream);
+  s = apply_layout(p, lay, B, H, true, true);
+  return s != ATTN_OK ? s : run_flash(p);
 }
 
 attn_variant attn_select(int B, int H, int Nq, int Nk, int d, attn_dtype dt, void* stream) {

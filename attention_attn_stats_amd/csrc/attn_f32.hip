@@ -70,8 +70,8 @@ __global__ __launch_bounds__(64 * kRows) void f32_kernel(const float* __restrict
                                                          const float* __restrict__ k,
                                                          const float* __restrict__ v,
                                                          float* __restrict__ out,
-                                                         float* __restrict__ ml, int BH, int Nq,
-                                                         int Nk, int D, float scale) {
+                                                         float* __restrict__ ml, const Layout lay,
+                                                         int BH, int Nq, int Nk, int D, float scale) {
   __shared__ float qs[kRows][kMaxD];
   __shared__ float ps[kRows][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -79,15 +79,17 @@ __global__ __launch_bounds__(64 * kRows) void f32_kernel(const float* __restrict
   const bool live = grow < (long long)BH * Nq;
   const int head = live ? (int)(grow / Nq) : 0;
   const int row = live ? (int)(grow - (long long)head * Nq) : 0;
-  const float* kh = k + (size_t)head * Nk * D;
-  const float* vh = v + (size_t)head * Nk * D;
-  for (int c = lane; c < D; c += 64) qs[wave][c] = live ? q[((size_t)head * Nq + row) * D + c] : 0.f;
+  const float* kh = k + head_offset(lay.k, lay.H, head);
+  const float* vh = MODE == kStats ? nullptr : v + head_offset(lay.v, lay.H, head);
+  const int kr = lay.k.row, vr_ = lay.v.row;
+  const float* qp = q + head_offset(lay.q, lay.H, head) + (size_t)row * lay.q.row;
+  for (int c = lane; c < D; c += 64) qs[wave][c] = live ? qp[c] : 0.f;
   __syncthreads();
 
   if constexpr (MODE == kStats) {
     Pair p{-INFINITY, 0.f};
     for (int j = lane; j < Nk; j += 64) {
-      const float a = logit(qs[wave], kh + (size_t)j * D, D, scale);
+      const float a = logit(qs[wave], kh + (size_t)j * kr, D, scale);
       p = merge(p, Pair{a, 1.f});
     }
     p = wave_merge(p);
@@ -105,7 +107,7 @@ __global__ __launch_bounds__(64 * kRows) void f32_kernel(const float* __restrict
     }
     for (int j0 = 0; j0 < Nk; j0 += 64) {
       const int j = j0 + lane;
-      const float a = j < Nk ? logit(qs[wave], kh + (size_t)j * D, D, scale) : -INFINITY;
+      const float a = j < Nk ? logit(qs[wave], kh + (size_t)j * kr, D, scale) : -INFINITY;
       float pj;
       if constexpr (MODE == kFlash) {
         const float mn = fmaxf(m, wave_max(a));  // finite: every chunk holds a key
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(64 * kRows) void f32_kernel(const float* __restrict
       const int nj = min(64, Nk - j0);
       for (int jj = 0; jj < nj; ++jj) {
         const float w = ps[wave][jj];
-        const float* vr = vh + (size_t)(j0 + jj) * D;
+        const float* vr = vh + (size_t)(j0 + jj) * vr_;
 #pragma unroll
         for (int t = 0; t < 3; ++t) {
           const int c = lane + 64 * t;
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(64 * kRows) void f32_kernel(const float* __restrict
     }
     if (live) {
       const float inv = 1.f / l;
-      float* op = out + ((size_t)head * Nq + row) * D;
+      float* op = out + head_offset(lay.o, lay.H, head) + (size_t)row * lay.o.row;
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
         const int c = lane + 64 * t;
@@ -154,7 +156,7 @@ hipError_t launch(const Problem& p) {
   if (blocks > 0x7fffffffLL || p.d > kMaxD) return hipErrorInvalidValue;
   hipLaunchKernelGGL((f32_kernel<MODE>), dim3((unsigned)blocks), dim3(64 * kRows), 0, p.stream,
                      (const float*)p.q, (const float*)p.k, (const float*)p.v, (float*)p.out, p.ml,
-                     p.BH, p.Nq, p.Nk, p.d, p.scale);
+                     p.lay, p.BH, p.Nq, p.Nk, p.d, p.scale);
   return hipGetLastError();
 }
 

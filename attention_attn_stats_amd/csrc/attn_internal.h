@@ -8,6 +8,30 @@
 
 namespace attn {
 
+// Element strides of a [B][H][N][d] tensor whose d elements are contiguous:
+// element (b, h, n, c) sits at b * batch + h * head + n * row + c.
+struct Strides {
+  long long batch, head;
+  int row;
+};
+// The four tensors' strides and the head count that splits a batch-major head
+// index bh into (bh / H, bh % H).
+struct Layout {
+  Strides q, k, v, o;
+  int H;
+};
+// Offset of head bh's first row.
+__host__ __device__ inline long long head_offset(const Strides& s, int H, int bh) {
+  return (long long)(bh / H) * s.batch + (long long)(bh % H) * s.head;
+}
+inline Strides dense_strides(int N, int d, int H) {
+  Strides s;
+  s.batch = (long long)H * N * d;
+  s.head = (long long)N * d;
+  s.row = d;
+  return s;
+}
+
 // One problem: BH independent heads of [Nq x d] queries against [Nk x d]
 // keys/values, all pointers device pointers, validated by the caller.
 struct Problem {
@@ -21,6 +45,7 @@ struct Problem {
   float scale;
   attn_dtype dt;
   hipStream_t stream;
+  Layout lay;  // strides of q, k, v, out (ml and a are always dense)
 };
 
 // Matrix-core (fp16 / bf16) kernels.

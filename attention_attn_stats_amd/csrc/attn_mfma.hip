@@ -213,7 +213,8 @@ __global__ __launch_bounds__(Shape<D>::T) void fwd_kernel(const uint16_t* __rest
                                                  const uint16_t* __restrict__ v,
                                                  uint16_t* __restrict__ out,
                                                  float* __restrict__ ml, const float* __restrict__ a,
-                                                 int Nq, int Nk, int qtiles, int nwg, float scale) {
+                                                 const Layout lay, int Nq, int Nk, int qtiles, int nwg,
+                                                 float scale) {
   using S = Shape<D>;
   constexpr int KS = S::KS, MT = S::MT, PK = S::PK, PV = S::PV, NBUF = S::NBUF;
   constexpr int BN = S::BN, NT = S::NT, kQG = S::QG, kHT = S::HT, kQWG = S::QWG;
@@ -250,9 +251,10 @@ __global__ __launch_bounds__(Shape<D>::T) void fwd_kernel(const uint16_t* __rest
   const int tile = xcd_tile(nwg);
   const int head = tile / qtiles;
   const int qbase = (tile - head * qtiles) * kQWG + qg * kQ;
-  const uint16_t* qh = q + (size_t)head * Nq * D;
-  const uint16_t* kh = k + (size_t)head * Nk * D;
-  const uint16_t* vh = kStats ? nullptr : v + (size_t)head * Nk * D;  // the stats form reads no V
+  const uint16_t* qh = q + head_offset(lay.q, lay.H, head);
+  const uint16_t* kh = k + head_offset(lay.k, lay.H, head);
+  const uint16_t* vh = kStats ? nullptr : v + head_offset(lay.v, lay.H, head);  // the stats form reads no V
+  const int qrs = lay.q.row, krs_ = lay.k.row, vrs_ = lay.v.row;  // row strides (elements)
   uint16_t* const ring = smem + half * NBUF * SLOT;
 
   if constexpr (S::kOnes) {
@@ -287,7 +289,7 @@ __global__ __launch_bounds__(Shape<D>::T) void fwd_kernel(const uint16_t* __rest
   } else {
     const int row = qbase + l32;
     const bool ok = row < Nq;
-    const uint16_t* qp = qh + (size_t)(ok ? row : 0) * D;
+    const uint16_t* qp = qh + (size_t)(ok ? row : 0) * qrs;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int d0 = ks * 16 + hi * 8;
@@ -332,12 +334,12 @@ __global__ __launch_bounds__(Shape<D>::T) void fwd_kernel(const uint16_t* __rest
     soff[r] = 0;
     if (j < KJOBS) {
       const int qi = 64 * j + lane, col = qi / BN, row = qi - col * BN;
-      goff[r] = (row * D + col * 8) * 2;
+      goff[r] = (row * krs_ + col * 8) * 2;
       soff[r] = row * PK + col * 8;
     } else if (j < NJOB) {
       const int qi = 64 * (j - KJOBS) + lane, row = qi / VCH, col = qi - row * VCH;
       if (row < BN && col < S::CPR) {
-        goff[r] = (vrow(row) * D + col * 8) * 2;
+        goff[r] = (vrow(row) * vrs_ + col * 8) * 2;
         soff[r] = BN * PK + row * PV + col * 8;
       }
     }
@@ -345,9 +347,11 @@ __global__ __launch_bounds__(Shape<D>::T) void fwd_kernel(const uint16_t* __rest
   uint4 stg[JPW];
   auto gload = [&](int it) {
     const int key0 = (2 * it + halfu) * BN;
-    const int bytes = (Nk > key0 ? Nk - key0 : 0) * D * 2;
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kh + (size_t)key0 * D, bytes);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vh + (size_t)key0 * D, bytes);
+    // the resources end after the last key's d elements
+    const int kbytes = Nk > key0 ? ((Nk - key0 - 1) * krs_ + D) * 2 : 0;
+    const int vbytes = Nk > key0 ? ((Nk - key0 - 1) * vrs_ + D) * 2 : 0;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kh + (size_t)key0 * krs_, kbytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc((kStats ? kh : vh) + (size_t)key0 * vrs_, kStats ? 0 : vbytes);
 #pragma unroll
     for (int r = 0; r < JPW; ++r) {
       const int j = qgu + kQG * r;
@@ -615,7 +619,7 @@ __global__ __launch_bounds__(Shape<D>::T) void fwd_kernel(const uint16_t* __rest
       }
     }
     if (row < Nq) {
-      uint16_t* op = out + ((size_t)head * Nq + row) * D;
+      uint16_t* op = out + head_offset(lay.o, lay.H, head) + (size_t)row * lay.o.row;
 #pragma unroll
       for (int mt = 0; mt < (kStats ? 0 : MT); ++mt) {
         const int dim = mt * 16 + G * 4;
@@ -645,7 +649,7 @@ hipError_t launch_fwd_t(const Problem& p) {
   if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((fwd_kernel<TR, D, MODE>), dim3((unsigned)nwg), dim3(Shape<D>::T), 0, p.stream,
                      (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v, (uint16_t*)p.out,
-                     p.ml, p.a, p.Nq, p.Nk, qtiles, (int)nwg, p.scale);
+                     p.ml, p.a, p.lay, p.Nq, p.Nk, qtiles, (int)nwg, p.scale);
   return hipGetLastError();
 }
 

@@ -58,8 +58,8 @@ constexpr int kSQ = 128, kSK = 128;  // tile of A per workgroup
 template <class TR, int D>
 __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict__ q,
                                                      const uint16_t* __restrict__ k,
-                                                     float* __restrict__ a, int Nq, int Nk, int qtiles,
-                                                     int ktiles, float scale) {
+                                                     float* __restrict__ a, const Layout lay, int Nq, int Nk,
+                                                     int qtiles, int ktiles, float scale) {
   constexpr int KS = (D + 15) / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -69,15 +69,16 @@ __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict_
   const int qt = t % qtiles;
   const int head = t / qtiles;
   const int q0 = qt * kSQ + wave * 32, k0 = kt * kSK;
-  const __amdgpu_buffer_rsrc_t qr = make_rsrc(q + (size_t)head * Nq * D, (uint32_t)Nq * D * 2);
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + (size_t)head * Nk * D, (uint32_t)Nk * D * 2);
+  const int qs = lay.q.row, ks_ = lay.k.row;  // row strides (elements)
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(q + head_offset(lay.q, lay.H, head), (uint32_t)((Nq - 1) * qs + D) * 2);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + head_offset(lay.k, lay.H, head), (uint32_t)((Nk - 1) * ks_ + D) * 2);
 
   // Q fragments: query q0 + l32, dims 16 ks + 8 hi .. +8 (zero past d)
   s8v qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const int d0 = ks * 16 + hi * 8;
-    const i4v x = __builtin_bit_cast(i4v, __builtin_amdgcn_raw_buffer_load_b128(qr, ((q0 + l32) * D + (d0 < D ? d0 : 0)) * 2, 0, 0));
+    const i4v x = __builtin_bit_cast(i4v, __builtin_amdgcn_raw_buffer_load_b128(qr, ((q0 + l32) * qs + (d0 < D ? d0 : 0)) * 2, 0, 0));
     qf[ks] = d0 < D ? __builtin_bit_cast(s8v, x) : (s8v){0, 0, 0, 0, 0, 0, 0, 0};
   }
   f16v acc[kSK / 32];
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict_
     for (int ks = 0; ks < KS; ++ks) {
       const int d0 = ks * 16 + hi * 8;
       // key k0 + 32 n + l32; past d the Q side is zero, so any finite data will do
-      const i4v x = __builtin_bit_cast(i4v, __builtin_amdgcn_raw_buffer_load_b128(kr, ((k0 + 32 * n + l32) * D + (d0 < D ? d0 : 0)) * 2, 0, 0));
+      const i4v x = __builtin_bit_cast(i4v, __builtin_amdgcn_raw_buffer_load_b128(kr, ((k0 + 32 * n + l32) * ks_ + (d0 < D ? d0 : 0)) * 2, 0, 0));
       acc[n] = TR::mma32(qf[ks], __builtin_bit_cast(s8v, x), acc[n]);
     }
   }
@@ -178,7 +179,7 @@ hipError_t launch_scores_t(const Problem& p, float* a) {
   const long long nwg = (long long)p.BH * qtiles * ktiles;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((scores_kernel<TR, D>), dim3((unsigned)nwg), dim3(256), 0, p.stream,
-                     (const uint16_t*)p.q, (const uint16_t*)p.k, a, p.Nq, p.Nk, qtiles, ktiles, p.scale);
+                     (const uint16_t*)p.q, (const uint16_t*)p.k, a, p.lay, p.Nq, p.Nk, qtiles, ktiles, p.scale);
   return hipGetLastError();
 }
 

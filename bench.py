@@ -60,13 +60,15 @@ def load_traffic(kernel: str, workload: str):
     return e.get("bytes_per_launch")
 
 
-def device_inputs(cfg):
+def device_inputs(cfg, layout: str = "bhnd"):
+    """q, k, v on the device: dense [B, H, N, d], or (layout 'bnhd') [B, H, N, d]
+    views of [B, N, H*d] tensors, the layout a UNet block's projections give."""
     import torch
-    from attention_attn_stats_amd import synth
     q, k, v = cfg.inputs()
     conv = {"f16": lambda a: torch.from_numpy(a), "f32": lambda a: torch.from_numpy(a),
             "bf16": lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16)}[cfg.dtype]
-    del synth
+    if layout == "bnhd":
+        return [conv(x.transpose(0, 2, 1, 3).copy()).cuda().transpose(1, 2) for x in (q, k, v)]
     return [conv(x).cuda().contiguous() for x in (q, k, v)]
 
 
@@ -123,7 +125,8 @@ def time_config(cfg, variant: str, steps: int, warmup: int):
 
 
 def algorithmic_bytes(cfg, form: str) -> dict:
-    """HBM bytes each form must move at least once (element size from dtype)."""
+    """HBM bytes each form must move at least once (element size from dtype);
+    the '_bnhd' forms move the same bytes as their dense forms."""
     es = {"f16": 2, "bf16": 2, "f32": 4}[cfg.dtype]
     bh = cfg.B * cfg.H
     q, kv, ml = bh * cfg.Nq * cfg.d * es, bh * cfg.Nk * cfg.d * es, bh * cfg.Nq * 8
@@ -131,18 +134,23 @@ def algorithmic_bytes(cfg, form: str) -> dict:
     pv = q + 2 * kv + ml + q                # pass 2: read Q, K, V, ml; write O
     a = bh * cfg.Nq * cfg.Nk * 4            # the stored logit matrix (float32)
     sc = {"scores": q + kv + a, "scores_stats": a + ml, "scores_pv": a + ml + kv + q}
-    return {"flash": q + 2 * kv + q, "pf": stats + pv, "stats": stats,
-            "pf_scores": sum(sc.values()), **sc}
+    r = {"flash": q + 2 * kv + q, "pf": stats + pv, "stats": stats,
+         "pf_scores": sum(sc.values()), **sc}
+    r.update({f"{f}_bnhd": r[f] for f in ("flash", "pf", "stats")})
+    return r
 
 
 def time_steps(cfg, form: str, steps: int, warmup: int, cold: bool):
     """Per-step times (ms) with events around every step, for the median / min
     of the configs table.  `cold` rewrites a 512 MiB buffer before every step
-    (outside the events) so that K and V come from HBM, not L2 / MALL."""
+    (outside the events) so that K and V come from HBM, not L2 / MALL.  A form
+    ending in '_bnhd' runs on [B, N, H*d] inputs and output (strided views)."""
     import statistics
     import torch
     import attention_attn_stats_amd as attn
-    q, k, v = device_inputs(cfg)
+    layout = "bnhd" if form.endswith("_bnhd") else "bhnd"
+    form = form[:-len("_bnhd")] if layout == "bnhd" else form
+    q, k, v = device_inputs(cfg, layout)
     out = torch.empty_like(q)
     ml = torch.empty((cfg.B, cfg.H, cfg.Nq, 2), device=q.device, dtype=torch.float32)
     a = (torch.empty((cfg.B, cfg.H, cfg.Nq, cfg.Nk), device=q.device, dtype=torch.float32)
@@ -199,7 +207,7 @@ def config_record(cfg, form: str, steps: int, cold: bool) -> dict:
            "pct_peak": round(100 * cfg.flops / (t["median_ms"] * 1e-3) / 1e12 / peak, 2),
            "algorithmic_bytes": by[form], "t_roof_us": round(t_roof * 1e6, 3),
            "roofline_frac": round(t_roof / (t["median_ms"] * 1e-3), 4)}
-    if form == "pf":
+    if form in ("pf", "pf_bnhd"):
         ts = t["first_kernel_median_ms"] * 1e-3
         rec["stats_pass_us"] = round(ts * 1e6, 2)
         rec["stats_pass_GBps"] = round(by["stats"] / ts / 1e9, 1)
@@ -258,7 +266,7 @@ def main():
     ap.add_argument("--config", default="sd512_self")
     ap.add_argument("--variant", default="auto", choices=["auto", "pf", "flash"])
     ap.add_argument("--forms", default="pf,flash,pf_scores",
-                    help="forms timed by --configs-out (pf, flash, pf_scores)")
+                    help="forms timed by --configs-out (pf, flash, pf_scores, pf_bnhd, flash_bnhd)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--configs-out", default=None)
     ap.add_argument("--cold", action="store_true")

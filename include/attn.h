@@ -113,6 +113,38 @@ attn_status attn_forward(const void* q, const void* k, const void* v, void* out,
                          int B, int H, int Nq, int Nk, int d, float scale, attn_variant var,
                          attn_dtype dt, void* stream);
 
+/* ---- Strided tensors -----------------------------------------------------
+ * The same four operations on q, k, v, out laid out with arbitrary element
+ * strides, e.g. the [B][N][H*d] activations of a UNet attention block viewed
+ * as [B][H][N][d] without a transpose (batch = N*H*d, head = d, row = H*d).
+ * Element (b, h, n, c) of a tensor is at b*batch + h*head + n*row + c; the d
+ * elements of a row are contiguous.  Requirements per tensor: strides >= 0,
+ * d <= row <= 2^20, all three strides multiples of 16 bytes (8 elements for
+ * F16/BF16, 4 for F32), one head's rows within 2^30 elements and the whole
+ * tensor within 2^31.  Strides of 0 share data (e.g. one k and v for every
+ * batch element) and are allowed for the inputs; out must overlap neither
+ * itself nor the inputs.  ml stays dense [B][H][Nq][2].  A NULL layout is the
+ * dense layout: each function above is its *_strided form with NULL.
+ * Violations return ATTN_ERR_INVALID_ARG before anything is launched. */
+typedef struct {
+  long long batch, head, row; /* element strides */
+} attn_strides;
+typedef struct {
+  attn_strides q, k, v, out; /* v and out are ignored where not used */
+} attn_layout;
+
+attn_status attn_stats_strided(const void* q, const void* k, float* ml, const attn_layout* layout, int B,
+                               int H, int Nq, int Nk, int d, float scale, attn_dtype dt, void* stream);
+attn_status attn_pv_strided(const void* q, const void* k, const void* v, const float* ml, void* out,
+                            const attn_layout* layout, int B, int H, int Nq, int Nk, int d, float scale,
+                            attn_dtype dt, void* stream);
+attn_status attn_flash_strided(const void* q, const void* k, const void* v, void* out, float* ml_out,
+                               const attn_layout* layout, int B, int H, int Nq, int Nk, int d, float scale,
+                               attn_dtype dt, void* stream);
+attn_status attn_forward_strided(const void* q, const void* k, const void* v, void* out, float* ml,
+                                 const attn_layout* layout, int B, int H, int Nq, int Nk, int d, float scale,
+                                 attn_variant var, attn_dtype dt, void* stream);
+
 /* ---- The partially fused softmax over a stored logit matrix ------------
  * The same two passes with A = scale * Q K^T written to memory first, as the
  * write-up draws the data flow (A is the input of the statistics pass and of

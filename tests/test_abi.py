@@ -112,3 +112,40 @@ def test_scores_entry_points_validation(lib):
     assert lib.attn_scores_pv(P, P, P, P + 8, 1, 1, 8, 8, 40, f, None) == _lib.ERR_INVALID_ARG
     assert lib.attn_scores_pv(P, P, P, P, 1, 1, 8, 8, 80, _lib.F32, None) == _lib.ERR_UNSUPPORTED
     assert lib.attn_scores_pv(P, P, P, P, 1, 1, 8, 8, 48, f, None) == _lib.ERR_UNSUPPORTED
+
+
+def _layout(row_q=40, row_k=40, row_v=40, row_o=40, head=0, batch=0):
+    S = _lib.Strides
+    return _lib.Layout(S(batch, head, row_q), S(batch, head, row_k), S(batch, head, row_v), S(batch, head, row_o))
+
+
+@pytest.mark.parametrize("lay", [
+    _layout(row_q=32),                 # row shorter than d
+    _layout(row_k=44),                 # row stride not a multiple of 16 bytes
+    _layout(head=-8),                  # negative stride
+    _layout(batch=4),                  # batch stride not a multiple of 16 bytes
+    _layout(row_v=1 << 27),            # one head's rows span more than 2^30 elements
+    _layout(row_o=36),                 # the output is checked too
+    _layout(row_k=(1 << 20) + 8),      # row stride past 2^20 elements (64-row blocks use 32-bit offsets)
+])
+def test_strided_layout_validation(lib, lay):
+    f = _lib.F16
+    r = ctypes.byref(lay)
+    assert lib.attn_flash_strided(P, P, P, P, None, r, 1, 1, 16, 16, 40, 0.1, f, None) == _lib.ERR_INVALID_ARG
+    assert lib.attn_forward_strided(P, P, P, P, P, r, 1, 1, 16, 16, 40, 0.1, _lib.AUTO, f, None) == \
+        _lib.ERR_INVALID_ARG
+    assert lib.attn_pv_strided(P, P, P, P, P, r, 1, 1, 16, 16, 40, 0.1, f, None) == _lib.ERR_INVALID_ARG
+
+
+def test_strided_stats_checks_only_q_and_k(lib):
+    f = _lib.F16
+    bad_q = _lib.Layout(_lib.Strides(0, 0, 36), _lib.Strides(0, 0, 40), _lib.Strides(), _lib.Strides())
+    assert lib.attn_stats_strided(P, P, P, ctypes.byref(bad_q), 1, 1, 8, 8, 40, 0.1, f, None) == \
+        _lib.ERR_INVALID_ARG
+    # f32 rows need 4-element (16-byte) multiples only
+    bad_f32 = _layout(row_q=42)
+    assert lib.attn_stats_strided(P, P, P, ctypes.byref(bad_f32), 1, 1, 8, 8, 40, 0.1, _lib.F32, None) == \
+        _lib.ERR_INVALID_ARG
+    # the plain checks still come first
+    assert lib.attn_stats_strided(None, P, P, None, 1, 1, 8, 8, 40, 0.1, f, None) == _lib.ERR_INVALID_ARG
+    assert lib.attn_stats_strided(P, P, P, None, 1, 1, 8, 8, 64, 0.1, f, None) == _lib.ERR_UNSUPPORTED
