@@ -53,8 +53,9 @@ def test_constant_v_rows_come_back(form, dtype, d):
 
 
 @pytest.mark.parametrize("form", FORMS)
-def test_zero_queries_average_v(form):
-    dtype, B, H, Nq, Nk, d = "f16", 2, 1, 64, 1000, 40
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_zero_queries_average_v(form, dtype):
+    B, H, Nq, Nk, d = 2, 1, 64, 1000, 40
     q = synth.round_to(np.zeros((B, H, Nq, d)), dtype)
     k = synth.tensor(21, (B, H, Nk, d), dtype)
     v = synth.tensor(22, (B, H, Nk, d), dtype)
@@ -68,9 +69,11 @@ def test_zero_queries_average_v(form):
 
 
 @pytest.mark.parametrize("form", FORMS)
-def test_key_shift_moves_m_only(form):
-    # values on a 1/64 grid in [-2, 2] and a shift of 0.5: every sum is exact in fp16
-    dtype, B, H, Nq, Nk, d = "f16", 1, 2, 96, 700, 40
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_key_shift_moves_m_only(form, dtype):
+    # values on a 1/64 grid in [-2, 2] and a shift of 0.5: every value and sum
+    # is a multiple of 1/64 below 4 in size, exact in fp16 and in bf16
+    B, H, Nq, Nk, d = 1, 2, 96, 700, 40
     grid = lambda seed, n: np.round(np.clip(synth.normal(seed, n), -2, 2) * 64) / 64
     q = synth.round_to(grid(31, B * H * Nq * d).reshape(B, H, Nq, d), dtype)
     k = synth.round_to(grid(32, B * H * Nk * d).reshape(B, H, Nk, d), dtype)
@@ -94,8 +97,9 @@ def test_key_shift_moves_m_only(form):
 
 @pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("where", [0, 517, 4095])
-def test_dominant_key_takes_the_weight(form, where):
-    dtype, B, H, Nq, Nk, d = "f16", 1, 1, 128, 4096, 40
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_dominant_key_takes_the_weight(form, where, dtype):
+    B, H, Nq, Nk, d = 1, 1, 128, 4096, 40
     q = synth.tensor(41, (B, H, Nq, d), dtype, 0.5)
     k = synth.tensor(42, (B, H, Nk, d), dtype, 0.5)
     v = synth.tensor(43, (B, H, Nk, d), dtype)
@@ -132,10 +136,11 @@ def test_rising_scores_rebase_every_block(form, dtype, d):
 
 
 @pytest.mark.parametrize("form", FORMS)
-def test_peaked_softmax_large_logits(form):
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_peaked_softmax_large_logits(form, dtype):
     # Q, K ~ N(0, 3^2): scores spread over hundreds, most weights underflow
     cfg = CONFIGS["level2_self"]
-    dtype, B, H, Nq, Nk, d = "f16", 1, 2, 256, 1024, 80
+    B, H, Nq, Nk, d = 1, 2, 256, 1024, 80
     q = synth.tensor(61, (B, H, Nq, d), dtype, 3.0)
     k = synth.tensor(62, (B, H, Nk, d), dtype, 3.0)
     v = synth.tensor(63, (B, H, Nk, d), dtype)

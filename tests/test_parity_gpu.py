@@ -62,10 +62,11 @@ def test_tiny_in_half_types(name, dtype):
 
 
 @pytest.mark.parametrize("name", LARGE)
-def test_full_size_sampled_rows(name):
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_full_size_sampled_rows(name, dtype):
     cfg = CONFIGS[name]
     rows = sample_rows(cfg.Nq, 48, seed=cfg.index)
-    _run_all(cfg, cfg.dtype, rows)
+    _run_all(cfg, dtype, rows)
 
 
 # Ragged and degenerate shapes: query counts that leave partial workgroup
