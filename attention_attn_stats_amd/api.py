@@ -213,6 +213,57 @@ def scores_pv(a, ml, v, out=None):
     return out
 
 
+_GN_WS = {}
+
+
+def _gn_workspace(device) -> torch.Tensor:
+    """One group-normalisation workspace per device and stream (kernels on one
+    stream never overlap, so they may share it)."""
+    key = (device, torch.cuda.current_stream(device).cuda_stream)
+    ws = _GN_WS.get(key)
+    if ws is None:
+        ws = torch.empty(_lib.GROUP_NORM_WORKSPACE_BYTES, dtype=torch.uint8, device=device)
+        _GN_WS[key] = ws
+    return ws
+
+
+def group_norm(x, groups: int, gamma=None, beta=None, eps: float = 1e-5, out=None, split: bool = True):
+    """Group normalisation of x [N, C, *spatial] (contiguous) with `groups`
+    groups of consecutive channels -> y of x's shape and dtype.  gamma, beta:
+    [C] in x's dtype or None.  out may be x (in place).  split=False keeps
+    every group on one workgroup (no workspace, no grid barrier)."""
+    if x.dim() < 2 or not x.is_cuda or not x.is_contiguous() or x.dtype not in _DT:
+        raise ValueError("x must be a contiguous [N, C, ...] device tensor of a supported dtype")
+    N, C = x.shape[:2]
+    HW = x.numel() // (N * C) if N * C else 0
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if t is not None and (t.shape != (C,) or t.dtype != x.dtype or not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous [C] device tensor of x's dtype")
+    out = torch.empty_like(x) if out is None else out
+    if out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous device tensor of x's shape and dtype")
+    ws = _gn_workspace(x.device) if split else None
+    _check(_lib.load().attn_group_norm(x.data_ptr(), gamma.data_ptr() if gamma is not None else None,
+                                       beta.data_ptr() if beta is not None else None, out.data_ptr(),
+                                       ws.data_ptr() if ws is not None else None, N, C, HW, int(groups),
+                                       float(eps), _DT[x.dtype], _stream()), "attn_group_norm")
+    return out
+
+
+def geglu(h, out=None):
+    """GELU-gated product of h [..., 2F] (contiguous): h[..., :F] * gelu(h[..., F:])."""
+    if h.dim() < 1 or not h.is_cuda or not h.is_contiguous() or h.dtype not in _DT or h.shape[-1] % 2:
+        raise ValueError("h must be a contiguous device tensor of a supported dtype with an even last dim")
+    F = h.shape[-1] // 2
+    rows = h.numel() // (2 * F) if F else 0
+    shape = tuple(h.shape[:-1]) + (F,)
+    out = torch.empty(shape, device=h.device, dtype=h.dtype) if out is None else out
+    if tuple(out.shape) != shape or out.dtype != h.dtype or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous device tensor [..., F] of h's dtype")
+    _check(_lib.load().attn_geglu(h.data_ptr(), out.data_ptr(), rows, F, _DT[h.dtype], _stream()), "attn_geglu")
+    return out
+
+
 def select(B, H, Nq, Nk, d, dtype=torch.float16) -> str:
     """The variant 'auto' uses for this shape ('pf' or 'flash'); may time both."""
     r = _lib.load().attn_select(B, H, Nq, Nk, d, _DT[dtype], _stream())

@@ -356,6 +356,55 @@ attn_status attn_flash_strided(const void* q, const void* k, const void* v, void
   return s != ATTN_OK ? s : run_flash(p);
 }
 
+// ---- group normalisation and the GELU-gated product ----------------------
+namespace {
+size_t elem_size(attn_dtype dt) { return dt == ATTN_F32 ? 4 : 2; }
+bool aligned_to(const void* p, size_t n) { return ((uintptr_t)p % n) == 0; }
+}  // namespace
+
+attn_status attn_group_norm(const void* x, const void* gamma, const void* beta, void* y, void* workspace,
+                            int N, int C, int HW, int G, float eps, attn_dtype dt, void* stream) {
+  if (dt != ATTN_F32 && dt != ATTN_F16 && dt != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!x || !y) return ATTN_ERR_INVALID_ARG;
+  if (N < 1 || C < 1 || HW < 1 || G < 1 || C % G != 0) return ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(eps) || eps < 0.f) return ATTN_ERR_INVALID_ARG;
+  if ((long long)N * C * HW >= (1LL << 40)) return ATTN_ERR_INVALID_ARG;
+  const size_t es = elem_size(dt);
+  if (!aligned_to(x, es) || !aligned_to(y, es) || (gamma && !aligned_to(gamma, es)) ||
+      (beta && !aligned_to(beta, es)) || (workspace && !aligned_to(workspace, 8)))
+    return ATTN_ERR_INVALID_ARG;
+  attn::GroupNormProblem p;
+  p.x = x;
+  p.gamma = gamma;
+  p.beta = beta;
+  p.y = y;
+  p.workspace = workspace;
+  p.N = N;
+  p.C = C;
+  p.HW = HW;
+  p.G = G;
+  p.eps = eps;
+  p.dt = dt;
+  p.stream = (hipStream_t)stream;
+  return to_status(attn::launch_group_norm(p));
+}
+
+attn_status attn_geglu(const void* h, void* out, int rows, int F, attn_dtype dt, void* stream) {
+  if (dt != ATTN_F32 && dt != ATTN_F16 && dt != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!h || !out || rows < 1 || F < 1) return ATTN_ERR_INVALID_ARG;
+  if ((long long)rows * F >= (1LL << 31) - 512) return ATTN_ERR_INVALID_ARG;
+  const size_t es = elem_size(dt);
+  if (!aligned_to(h, es) || !aligned_to(out, es)) return ATTN_ERR_INVALID_ARG;
+  attn::GegluProblem p;
+  p.h = h;
+  p.out = out;
+  p.rows = rows;
+  p.F = F;
+  p.dt = dt;
+  p.stream = (hipStream_t)stream;
+  return to_status(attn::launch_geglu(p));
+}
+
 attn_variant attn_select(int B, int H, int Nq, int Nk, int d, attn_dtype dt, void* stream) {
   if (check_common(B, H, Nq, Nk, d, 1.f, dt) != ATTN_OK) return ATTN_AUTO;
   const attn_variant forced = env_override();

@@ -58,6 +58,31 @@ hipError_t launch_scores(const Problem& p, float* a);                   // A = s
 hipError_t launch_scores_stats(const float* a, float* ml, long long rows, int Nk, hipStream_t stream);
 hipError_t launch_mfma_pv_scores(const Problem& p);                     // O from p.a, p.ml, p.v
 
+// Group normalisation of x [N][C][HW] (y may equal x); workspace may be null.
+constexpr size_t kGroupNormWorkspaceBytes = ATTN_GROUP_NORM_WORKSPACE_BYTES;
+struct GroupNormProblem {
+  const void* x;
+  const void* gamma;
+  const void* beta;
+  void* y;
+  void* workspace;
+  int N, C, HW, G;
+  float eps;
+  attn_dtype dt;
+  hipStream_t stream;
+};
+hipError_t launch_group_norm(const GroupNormProblem& p);
+
+// GELU-gated product: h [rows][2F] -> out [rows][F].
+struct GegluProblem {
+  const void* h;
+  void* out;
+  int rows, F;
+  attn_dtype dt;
+  hipStream_t stream;
+};
+hipError_t launch_geglu(const GegluProblem& p);
+
 // Vector-ALU float32 kernels.
 hipError_t launch_f32_stats(const Problem& p);
 hipError_t launch_f32_pv(const Problem& p);

@@ -173,6 +173,41 @@ attn_status attn_scores_stats(const float* a, float* ml, int B, int H, int Nq, i
 attn_status attn_scores_pv(const float* a, const float* ml, const void* v, void* out, int B, int H, int Nq,
                            int Nk, int d, attn_dtype dt, void* stream);
 
+/* ---- The two other specialised kernels of the UNet ------------------------
+ * "Speed Is All You Need" (Chen et al.), news write-up, section on the
+ * specialised kernels: group normalisation as one GPU command with no
+ * intermediate tensor, and GELU evaluated with the error function in one pass
+ * together with the split and the multiplication around it. */
+
+/* Bytes of the optional group-normalisation workspace (device memory, 8-byte
+ * aligned, contents need no initialisation; calls sharing one workspace must
+ * not overlap in time). */
+#define ATTN_GROUP_NORM_WORKSPACE_BYTES 131072
+
+/* Group normalisation of x [N][C][HW] (NCHW, spatial dims flattened) with G
+ * groups of C/G consecutive channels: per (n, g) the mean and the biased
+ * variance over the group's (C/G)*HW elements, then
+ * y = (x - mean) / sqrt(var + eps) * gamma[c] + beta[c].  Statistics in
+ * float32 (pairwise merged moments, never sums of squares).  gamma, beta: [C]
+ * in dt, or NULL for 1 and 0.  y [N][C][HW] in dt, written; y may equal x.
+ * One launch.  With a workspace, large groups are split over several
+ * workgroups that exchange their moments at a grid barrier (a cooperative
+ * launch); with NULL, each group is one workgroup.  Requirements: sizes >= 1,
+ * C a multiple of G, eps finite and >= 0, pointers aligned to the element
+ * size, N*C*HW < 2^40.  Violations return ATTN_ERR_INVALID_ARG before anything
+ * is launched. */
+attn_status attn_group_norm(const void* x, const void* gamma, const void* beta, void* y, void* workspace,
+                            int N, int C, int HW, int G, float eps, attn_dtype dt, void* stream);
+
+/* GELU-gated product: h [rows][2F] -> out [rows][F],
+ * out[r][j] = h[r][j] * gelu(h[r][F + j]), gelu(g) = g Phi(g) =
+ * g (1 + erf(g / sqrt 2)) / 2 (the exact form), float32 arithmetic.  The
+ * first half of a row is the value, the second half the gate.  h read only,
+ * out written (must not overlap h).  Requirements: rows, F >= 1,
+ * rows*F < 2^31 - 2^9, pointers aligned to the element size; else
+ * ATTN_ERR_INVALID_ARG. */
+attn_status attn_geglu(const void* h, void* out, int rows, int F, attn_dtype dt, void* stream);
+
 /* The variant ATTN_AUTO uses for this shape.  On a cache miss it allocates
  * temporary device buffers, times both variants on `stream`, frees the
  * buffers and caches the winner, so it synchronises and may allocate; call it

@@ -149,3 +149,32 @@ def test_strided_stats_checks_only_q_and_k(lib):
     # the plain checks still come first
     assert lib.attn_stats_strided(None, P, P, None, 1, 1, 8, 8, 40, 0.1, f, None) == _lib.ERR_INVALID_ARG
     assert lib.attn_stats_strided(P, P, P, None, 1, 1, 8, 8, 64, 0.1, f, None) == _lib.ERR_UNSUPPORTED
+
+
+def test_group_norm_and_geglu_validation(lib):
+    f = _lib.F16
+    # attn_group_norm(x, gamma, beta, y, workspace, N, C, HW, G, eps, dt, stream)
+    gn = lib.attn_group_norm
+    assert gn(None, None, None, P, P, 2, 32, 64, 32, 1e-5, f, None) == _lib.ERR_INVALID_ARG
+    assert gn(P, None, None, None, P, 2, 32, 64, 32, 1e-5, f, None) == _lib.ERR_INVALID_ARG
+    assert gn(P, None, None, P, P, 2, 30, 64, 4, 1e-5, f, None) == _lib.ERR_INVALID_ARG      # C % G
+    assert gn(P, None, None, P, P, 0, 32, 64, 32, 1e-5, f, None) == _lib.ERR_INVALID_ARG     # N
+    assert gn(P, None, None, P, P, 2, 32, 0, 32, 1e-5, f, None) == _lib.ERR_INVALID_ARG      # HW
+    assert gn(P, None, None, P, P, 2, 32, 64, 0, 1e-5, f, None) == _lib.ERR_INVALID_ARG      # G
+    assert gn(P, None, None, P, P, 2, 32, 64, 32, -1.0, f, None) == _lib.ERR_INVALID_ARG     # eps
+    assert gn(P, None, None, P, P, 2, 32, 64, 32, float("nan"), f, None) == _lib.ERR_INVALID_ARG
+    assert gn(P + 1, None, None, P, P, 2, 32, 64, 32, 1e-5, f, None) == _lib.ERR_INVALID_ARG  # x alignment
+    assert gn(P, P + 1, None, P, P, 2, 32, 64, 32, 1e-5, f, None) == _lib.ERR_INVALID_ARG     # gamma alignment
+    assert gn(P, None, None, P, P + 4, 2, 32, 64, 32, 1e-5, f, None) == _lib.ERR_INVALID_ARG  # workspace alignment
+    assert gn(P + 2, None, None, P, P, 2, 32, 64, 32, 1e-5, _lib.F32, None) == _lib.ERR_INVALID_ARG
+    assert gn(P, None, None, P, P, 1 << 16, 1 << 12, 1 << 12, 32, 1e-5, f, None) == _lib.ERR_INVALID_ARG
+    assert gn(P, None, None, P, P, 2, 32, 64, 32, 1e-5, 9, None) == _lib.ERR_UNSUPPORTED
+    # attn_geglu(h, out, rows, F, dt, stream)
+    ge = lib.attn_geglu
+    assert ge(None, P, 4, 8, f, None) == _lib.ERR_INVALID_ARG
+    assert ge(P, None, 4, 8, f, None) == _lib.ERR_INVALID_ARG
+    assert ge(P, P, 0, 8, f, None) == _lib.ERR_INVALID_ARG
+    assert ge(P, P, 4, 0, f, None) == _lib.ERR_INVALID_ARG
+    assert ge(P + 1, P, 4, 8, f, None) == _lib.ERR_INVALID_ARG
+    assert ge(P, P, 1 << 16, 1 << 15, f, None) == _lib.ERR_INVALID_ARG  # rows * F >= 2^31 - 512
+    assert ge(P, P, 4, 8, 9, None) == _lib.ERR_UNSUPPORTED
