@@ -216,22 +216,21 @@ def scores_pv(a, ml, v, out=None):
 _GN_WS = {}
 
 
-def _gn_workspace(device) -> torch.Tensor:
-    """One group-normalisation workspace per device and stream (kernels on one
-    stream never overlap, so they may share it)."""
+def _gn_workspace(device, nbytes: int) -> torch.Tensor:
+    """A group-normalisation workspace of at least nbytes, one per device and
+    stream (kernels on one stream never overlap, so they may share it)."""
     key = (device, torch.cuda.current_stream(device).cuda_stream)
     ws = _GN_WS.get(key)
-    if ws is None:
-        ws = torch.empty(_lib.GROUP_NORM_WORKSPACE_BYTES, dtype=torch.uint8, device=device)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
         _GN_WS[key] = ws
     return ws
 
 
-def group_norm(x, groups: int, gamma=None, beta=None, eps: float = 1e-5, out=None, split: bool = True):
+def group_norm(x, groups: int, gamma=None, beta=None, eps: float = 1e-5, out=None):
     """Group normalisation of x [N, C, *spatial] (contiguous) with `groups`
     groups of consecutive channels -> y of x's shape and dtype.  gamma, beta:
-    [C] in x's dtype or None.  out may be x (in place).  split=False keeps
-    every group on one workgroup (no workspace, no grid barrier)."""
+    [C] in x's dtype or None.  out may be x (in place)."""
     if x.dim() < 2 or not x.is_cuda or not x.is_contiguous() or x.dtype not in _DT:
         raise ValueError("x must be a contiguous [N, C, ...] device tensor of a supported dtype")
     N, C = x.shape[:2]
@@ -242,11 +241,13 @@ def group_norm(x, groups: int, gamma=None, beta=None, eps: float = 1e-5, out=Non
     out = torch.empty_like(x) if out is None else out
     if out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous() or not out.is_cuda:
         raise ValueError("out must be a contiguous device tensor of x's shape and dtype")
-    ws = _gn_workspace(x.device) if split else None
-    _check(_lib.load().attn_group_norm(x.data_ptr(), gamma.data_ptr() if gamma is not None else None,
-                                       beta.data_ptr() if beta is not None else None, out.data_ptr(),
-                                       ws.data_ptr() if ws is not None else None, N, C, HW, int(groups),
-                                       float(eps), _DT[x.dtype], _stream()), "attn_group_norm")
+    lib = _lib.load()
+    need = lib.attn_group_norm_workspace_size(x.data_ptr(), out.data_ptr(), N, C, HW, int(groups), _DT[x.dtype])
+    ws = _gn_workspace(x.device, need) if need else None
+    _check(lib.attn_group_norm(x.data_ptr(), gamma.data_ptr() if gamma is not None else None,
+                               beta.data_ptr() if beta is not None else None, out.data_ptr(),
+                               ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
+                               N, C, HW, int(groups), float(eps), _DT[x.dtype], _stream()), "attn_group_norm")
     return out
 
 

@@ -362,31 +362,55 @@ size_t elem_size(attn_dtype dt) { return dt == ATTN_F32 ? 4 : 2; }
 bool aligned_to(const void* p, size_t n) { return ((uintptr_t)p % n) == 0; }
 }  // namespace
 
-attn_status attn_group_norm(const void* x, const void* gamma, const void* beta, void* y, void* workspace,
-                            int N, int C, int HW, int G, float eps, attn_dtype dt, void* stream) {
+namespace {
+// Validates a group-normalisation problem and fills p (all but the workspace).
+attn_status gn_problem(const void* x, const void* gamma, const void* beta, void* y, int N, int C, int HW, int G,
+                       float eps, attn_dtype dt, void* stream, attn::GroupNormProblem* p) {
   if (dt != ATTN_F32 && dt != ATTN_F16 && dt != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (!x || !y) return ATTN_ERR_INVALID_ARG;
   if (N < 1 || C < 1 || HW < 1 || G < 1 || C % G != 0) return ATTN_ERR_INVALID_ARG;
   if (!std::isfinite(eps) || eps < 0.f) return ATTN_ERR_INVALID_ARG;
-  if ((long long)N * C * HW >= (1LL << 40)) return ATTN_ERR_INVALID_ARG;
+  if ((long long)N * C * HW >= (1LL << 40) || (long long)(C / G) * HW >= 0x7fffffffLL) return ATTN_ERR_INVALID_ARG;
   const size_t es = elem_size(dt);
   if (!aligned_to(x, es) || !aligned_to(y, es) || (gamma && !aligned_to(gamma, es)) ||
-      (beta && !aligned_to(beta, es)) || (workspace && !aligned_to(workspace, 8)))
+      (beta && !aligned_to(beta, es)))
     return ATTN_ERR_INVALID_ARG;
+  p->x = x;
+  p->gamma = gamma;
+  p->beta = beta;
+  p->y = y;
+  p->workspace = nullptr;
+  p->workspace_bytes = 0;
+  p->N = N;
+  p->C = C;
+  p->HW = HW;
+  p->G = G;
+  p->eps = eps;
+  p->dt = dt;
+  p->stream = (hipStream_t)stream;
+  return ATTN_OK;
+}
+}  // namespace
+
+attn_status attn_group_norm(const void* x, const void* gamma, const void* beta, void* y, void* workspace,
+                            size_t workspace_bytes, int N, int C, int HW, int G, float eps, attn_dtype dt,
+                            void* stream) {
   attn::GroupNormProblem p;
-  p.x = x;
-  p.gamma = gamma;
-  p.beta = beta;
-  p.y = y;
+  attn_status s = gn_problem(x, gamma, beta, y, N, C, HW, G, eps, dt, stream, &p);
+  if (s != ATTN_OK) return s;
+  if (workspace && !aligned_to(workspace, 8)) return ATTN_ERR_INVALID_ARG;
+  const size_t need = attn::group_norm_workspace(p);
+  if (need && (!workspace || workspace_bytes < need)) return ATTN_ERR_INVALID_ARG;
   p.workspace = workspace;
-  p.N = N;
-  p.C = C;
-  p.HW = HW;
-  p.G = G;
-  p.eps = eps;
-  p.dt = dt;
-  p.stream = (hipStream_t)stream;
+  p.workspace_bytes = workspace ? workspace_bytes : 0;
   return to_status(attn::launch_group_norm(p));
+}
+
+size_t attn_group_norm_workspace_size(const void* x, const void* y, int N, int C, int HW, int G,
+                                      attn_dtype dt) {
+  attn::GroupNormProblem p;
+  if (gn_problem(x, nullptr, nullptr, const_cast<void*>(y), N, C, HW, G, 0.f, dt, nullptr, &p) != ATTN_OK) return 0;
+  return attn::group_norm_workspace(p);
 }
 
 attn_status attn_geglu(const void* h, void* out, int rows, int F, attn_dtype dt, void* stream) {

@@ -58,19 +58,21 @@ hipError_t launch_scores(const Problem& p, float* a);                   // A = s
 hipError_t launch_scores_stats(const float* a, float* ml, long long rows, int Nk, hipStream_t stream);
 hipError_t launch_mfma_pv_scores(const Problem& p);                     // O from p.a, p.ml, p.v
 
-// Group normalisation of x [N][C][HW] (y may equal x); workspace may be null.
-constexpr size_t kGroupNormWorkspaceBytes = ATTN_GROUP_NORM_WORKSPACE_BYTES;
+// Group normalisation of x [N][C][HW] (y may equal x).  The workspace is
+// needed only by groups too large for one workgroup's registers.
 struct GroupNormProblem {
   const void* x;
   const void* gamma;
   const void* beta;
   void* y;
   void* workspace;
+  size_t workspace_bytes;
   int N, C, HW, G;
   float eps;
   attn_dtype dt;
   hipStream_t stream;
 };
+size_t group_norm_workspace(const GroupNormProblem& p);  // bytes the launch plan needs (0: none)
 hipError_t launch_group_norm(const GroupNormProblem& p);
 
 // GELU-gated product: h [rows][2F] -> out [rows][F].

@@ -10,18 +10,17 @@
 // all spatial positions (biased variance, eps inside the square root, then a
 // per-channel affine), gelu(g) = g Phi(g) with the error function, and
 // out = value * gelu(gate) with the value in the first half of a row.
-#include <hip/hip_cooperative_groups.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <mutex>
+#include <cstdlib>
+#include <cstring>
+#include <type_traits>
 
 #include "attn_internal.h"
 
 namespace attn {
 namespace {
-
-namespace cg = cooperative_groups;
 
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef __bf16 b8v __attribute__((ext_vector_type(8)));
@@ -77,29 +76,39 @@ struct EF32 {
 
 // ---------------------------------------------------------------------------
 // Group normalisation.  x, y: [N][C][HW], so group (n, g) is one contiguous
-// span of L = (C/G) HW elements.  Every group is cut into S slices of
-// consecutive 16-byte vectors, one workgroup per slice.  A workgroup reduces
-// its slice to (count, mean, M2) -- per thread, then across the workgroup with
-// the pairwise update (n, m, M2) + (n', m', M2') = (n + n', m + d n'/(n + n'),
-// M2 + M2' + d^2 n n'/(n + n')), d = m' - m -- and, when S > 1, publishes the
-// pair in a small workspace, waits at a grid barrier (cooperative launch: all
-// workgroups are resident) and merges its group's S pairs in slice order, so
-// every workgroup of a group derives the same mean and 1/sqrt(var + eps).  It
-// then writes its slice.  With kResident the slice stays in registers between
-// the two phases (x is read once); otherwise it is read a second time.
+// span of L = (C/G) HW elements, cut into 16-byte vectors of VW elements
+// (HW a multiple of VW keeps every vector inside one channel).
+//
+// Moments (count, mean, M2 = sum of squared deviations) are reduced per
+// thread with two passes over the thread's own values, then merged pairwise,
+// (n, m, M2) + (n', m', M2') = (n + n', m + d n'/(n + n'),
+// M2 + M2' + d^2 n n'/(n + n')), d = m' - m, in a fixed order, so results are
+// deterministic and never rely on E[x^2] - E[x]^2.
+//
+// One launch (gn_fused_kernel) whenever a group fits one workgroup's
+// registers: 1024 threads hold up to 16 vectors each (131072 fp16/bf16 or
+// 65536 fp32 elements), every load of the group is issued before the first
+// is used, the moments are merged across the workgroup, and the group is
+// written from registers -- x read once, y written once, no intermediate
+// tensor.  Larger groups take two launches over S slices per group: the
+// first writes each slice's moments to a small workspace, the second merges
+// its group's S moments (in slice order, identically in every workgroup) and
+// normalises its slice, reading x a second time.
 // ---------------------------------------------------------------------------
-constexpr int kGnThreads = 256;
-constexpr int kGnResidentVecs = 4;  // 16-byte vectors per thread kept in registers
+constexpr int kGnFusedThreads = 1024, kGnMaxRv = 16;
+constexpr int kGnSliceThreads = 256, kGnSliceBatch = 4;  // vectors in flight per thread when streaming
+constexpr long long kGnSliceTarget = 512;                  // workgroups the two-launch path aims for
+constexpr long long kGnFusedMinGroups = 256;               // groups that fill the chip in one launch
 
 struct GnArgs {
   const void* x;
   const void* gamma;  // [C] or null
   const void* beta;   // [C] or null
   void* y;
-  float2* ws;          // [grid] (mean, M2) per slice, used when S > 1
+  float2* ws;          // [groups][S] (mean, M2) per slice (two-launch path)
   long long L;         // elements per group
   long long slice_vec; // vectors per slice (the last slice of a group may be shorter)
-  int C, HW, G, Cg, S;
+  int HW, G, Cg, S;
   float eps;
 };
 
@@ -108,29 +117,28 @@ struct Moments {
 };
 
 __device__ __forceinline__ void merge(Moments& a, const Moments& b) {
-  const float n = a.n + b.n;
   if (b.n == 0.f) return;
   if (a.n == 0.f) {
     a = b;
     return;
   }
-  const float d = b.mean - a.mean, f = b.n / n;
+  const float n = a.n + b.n;
+  const float d = b.mean - a.mean, f = b.n * __builtin_amdgcn_rcpf(n);  // 1-ulp reciprocal
   a.mean += d * f;
   a.m2 += b.m2 + d * d * a.n * f;
   a.n = n;
 }
 
-// Moments of the workgroup's threads, merged in a fixed order; the result is
-// returned to every thread.
-__device__ Moments block_merge(Moments t, Moments* lds) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Merge across the 64 lanes of a wave; lane 0 ends with the lanes merged in
+// one fixed order (the lower lane's side first at every step).
+__device__ __forceinline__ Moments wave_merge(Moments t) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     Moments o;
     o.n = __shfl_xor(t.n, off);
     o.mean = __shfl_xor(t.mean, off);
     o.m2 = __shfl_xor(t.m2, off);
-    // the lower lane keeps its own side first: lane 0 ends with one fixed order
     if (lane & off) {
       Moments s = o;
       merge(s, t);
@@ -139,243 +147,316 @@ __device__ Moments block_merge(Moments t, Moments* lds) {
       merge(t, o);
     }
   }
-  if (lane == 0) lds[wave] = t;
+  return t;
+}
+
+// Moments of the workgroup's threads (NT threads), the same on every thread.
+template <int NT>
+__device__ Moments block_merge(Moments t, Moments* lds) {
+  t = wave_merge(t);
+  if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = t;
   __syncthreads();
   Moments r = lds[0];
 #pragma unroll
-  for (int w = 1; w < kGnThreads / 64; ++w) merge(r, lds[w]);
-  __syncthreads();  // lds may be reused
+  for (int w = 1; w < NT / 64; ++w) merge(r, lds[w]);
   return r;
 }
 
 template <class E, bool kVec>
 struct GnIo {
   static constexpr int VW = kVec ? E::VW : 1;
-  // vector v of a group starting at element `base`: VW floats
-  static __device__ __forceinline__ void load(const void* x, size_t base, long long v, float* f) {
-    if constexpr (kVec) {
-      E::unpack(*(const uint4*)((const char*)x + (base + (size_t)v * VW) * sizeof_elem()), f);
-    } else {
-      f[0] = E::get(x, base + (size_t)v);
-    }
+  static constexpr size_t ES = 16 / E::VW;  // element size
+  // vector v of the group starting at element `base`, raw
+  using Raw = typename std::conditional<kVec, uint4, float>::type;
+  static __device__ __forceinline__ Raw load(const void* x, size_t base, long long v) {
+    if constexpr (kVec)
+      return *(const uint4*)((const char*)x + (base + (size_t)v * VW) * ES);
+    else
+      return E::get(x, base + (size_t)v);
+  }
+  static __device__ __forceinline__ void unpack(const Raw& r, float* f) {
+    if constexpr (kVec)
+      E::unpack(r, f);
+    else
+      f[0] = r;
   }
   static __device__ __forceinline__ void store(void* y, size_t base, long long v, const float* f) {
-    if constexpr (kVec) {
-      *(uint4*)((char*)y + (base + (size_t)v * VW) * sizeof_elem()) = E::pack(f);
-    } else {
+    if constexpr (kVec)
+      *(uint4*)((char*)y + (base + (size_t)v * VW) * ES) = E::pack(f);
+    else
       E::put(y, base + (size_t)v, f[0]);
-    }
   }
-  static __device__ __forceinline__ constexpr size_t sizeof_elem() { return 16 / E::VW; }
 };
 
-template <class E, bool kSplit, bool kResident, bool kVec>
-__global__ __launch_bounds__(kGnThreads) void group_norm_kernel(const GnArgs a) {
+// y = x a_c + b_c for vector v of the group, a_c = rstd gamma_c,
+// b_c = beta_c - mean a_c (every element of a vector is in channel c).
+template <class E, bool kVec>
+__device__ __forceinline__ void gn_write(const GnArgs& a, int gin, size_t base, long long v, float* f, float mean,
+                                         float rstd) {
+  using IO = GnIo<E, kVec>;
+  // the group's elements number below 2^31 (checked at launch): 32-bit division
+  const int c = gin * a.Cg + (int)((unsigned)(v * IO::VW) / (unsigned)a.HW);
+  const float ga = a.gamma ? E::get(a.gamma, c) : 1.f;
+  const float be = a.beta ? E::get(a.beta, c) : 0.f;
+  const float sc = rstd * ga, sh = be - mean * sc;
+#pragma unroll
+  for (int i = 0; i < IO::VW; ++i) f[i] = __builtin_fmaf(f[i], sc, sh);
+  IO::store(a.y, base, v, f);
+}
+
+template <class E, bool kVec, int RV>
+__global__ __launch_bounds__(kGnFusedThreads) void gn_fused_kernel(const GnArgs a) {
   using IO = GnIo<E, kVec>;
   constexpr int VW = IO::VW;
-  __shared__ Moments lds[kGnThreads / 64];
-  __shared__ float2 coef;  // (mean, rstd) of the group
+  __shared__ Moments lds[kGnFusedThreads / 64];
   const int tid = threadIdx.x;
-  const int grp = blockIdx.x / a.S, sl = blockIdx.x - grp * a.S;
-  const size_t base = (size_t)grp * a.L;  // first element of the group
-  const long long lv = a.L / VW;          // vectors per group
-  const long long v0 = (long long)sl * a.slice_vec;
-  const long long v1 = v0 + a.slice_vec < lv ? v0 + a.slice_vec : lv;
-
-  // phase 1: moments of this thread's vectors (each vector reduced on its
-  // own first, then merged), then of the workgroup
-  float xr[kResident ? kGnResidentVecs : 1][VW];
-  Moments t = {0.f, 0.f, 0.f};
-  auto add_vector = [&](const float* f) {
-    float s = 0.f;
+  const int grp = blockIdx.x;
+  const size_t base = (size_t)grp * a.L;
+  const long long lv = a.L / VW;
+  typename IO::Raw raw[RV];
 #pragma unroll
-    for (int i = 0; i < VW; ++i) s += f[i];
-    Moments m;
-    m.n = (float)VW;
-    m.mean = s * (1.f / VW);
-    m.m2 = 0.f;
+  for (int k = 0; k < RV; ++k) {
+    const long long v = tid + (long long)k * kGnFusedThreads;
+    if (v < lv) raw[k] = IO::load(a.x, base, v);
+  }
+  // this thread's moments: mean first, then squared deviations
+  float n = 0.f, s = 0.f;
 #pragma unroll
-    for (int i = 0; i < VW; ++i) m.m2 += (f[i] - m.mean) * (f[i] - m.mean);
-    merge(t, m);
-  };
-  if constexpr (kResident) {
-#pragma unroll
-    for (int k = 0; k < kGnResidentVecs; ++k) {
-      const long long v = v0 + tid + (long long)k * kGnThreads;
-      if (v < v1) IO::load(a.x, base, v, xr[k]);
-    }
-#pragma unroll
-    for (int k = 0; k < kGnResidentVecs; ++k)
-      if (v0 + tid + (long long)k * kGnThreads < v1) add_vector(xr[k]);
-  } else {
-    for (long long v = v0 + tid; v < v1; v += kGnThreads) {
+  for (int k = 0; k < RV; ++k) {
+    if (tid + (long long)k * kGnFusedThreads < lv) {
       float f[VW];
-      IO::load(a.x, base, v, f);
-      add_vector(f);
+      IO::unpack(raw[k], f);
+#pragma unroll
+      for (int i = 0; i < VW; ++i) s += f[i];
+      n += (float)VW;
     }
   }
-  const Moments wg = block_merge(t, lds);
-
-  if (tid == 0 && !kSplit) coef = make_float2(wg.mean, 1.f / __builtin_sqrtf(wg.m2 / (float)a.L + a.eps));
-  if constexpr (kSplit) {
-    if (tid == 0) a.ws[blockIdx.x] = make_float2(wg.mean, wg.m2);
-    cg::this_grid().sync();
-    if (tid < 64) {
-      // lane j merges slices j, j + 64, ... of the group in order, then the
-      // lanes merge pairwise; lane 0 holds the group's moments
-      Moments g = {0.f, 0.f, 0.f};
-      for (int s = tid; s < a.S; s += 64) {
-        const float2 p = a.ws[(size_t)grp * a.S + s];
-        const long long s0 = (long long)s * a.slice_vec;
-        const long long s1 = s0 + a.slice_vec < lv ? s0 + a.slice_vec : lv;
-        Moments m = {(float)((s1 - s0) * VW), p.x, p.y};
-        merge(g, m);
-      }
+  Moments t = {n, n > 0.f ? s / n : 0.f, 0.f};
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        Moments o;
-        o.n = __shfl_xor(g.n, off);
-        o.mean = __shfl_xor(g.mean, off);
-        o.m2 = __shfl_xor(g.m2, off);
-        if (tid & off) {
-          Moments s = o;
-          merge(s, g);
-          g = s;
-        } else {
-          merge(g, o);
-        }
-      }
-      if (tid == 0) coef = make_float2(g.mean, 1.f / __builtin_sqrtf(g.m2 / (float)a.L + a.eps));
+  for (int k = 0; k < RV; ++k) {
+    if (tid + (long long)k * kGnFusedThreads < lv) {
+      float f[VW];
+      IO::unpack(raw[k], f);
+#pragma unroll
+      for (int i = 0; i < VW; ++i) t.m2 += (f[i] - t.mean) * (f[i] - t.mean);
     }
+  }
+  const Moments g = block_merge<kGnFusedThreads>(t, lds);
+  const float rstd = 1.f / __builtin_sqrtf(g.m2 / (float)a.L + a.eps);
+  const int gin = grp % a.G;
+#pragma unroll
+  for (int k = 0; k < RV; ++k) {
+    const long long v = tid + (long long)k * kGnFusedThreads;
+    if (v < lv) {
+      float f[VW];
+      IO::unpack(raw[k], f);
+      gn_write<E, kVec>(a, gin, base, v, f, g.mean, rstd);
+    }
+  }
+}
+
+// Two-launch path, first launch: the moments of every slice.
+template <class E, bool kVec>
+__global__ __launch_bounds__(kGnSliceThreads) void gn_partial_kernel(const GnArgs a) {
+  using IO = GnIo<E, kVec>;
+  constexpr int VW = IO::VW;
+  __shared__ Moments lds[kGnSliceThreads / 64];
+  const int grp = blockIdx.x / a.S, sl = blockIdx.x - grp * a.S;
+  const size_t base = (size_t)grp * a.L;
+  const long long lv = a.L / VW;
+  const long long v0 = (long long)sl * a.slice_vec;
+  const long long v1 = v0 + a.slice_vec < lv ? v0 + a.slice_vec : lv;
+  Moments t = {0.f, 0.f, 0.f};
+  for (long long vb = v0 + threadIdx.x; vb < v1; vb += (long long)kGnSliceThreads * kGnSliceBatch) {
+    typename IO::Raw raw[kGnSliceBatch];
+#pragma unroll
+    for (int k = 0; k < kGnSliceBatch; ++k) {
+      const long long v = vb + (long long)k * kGnSliceThreads;
+      if (v < v1) raw[k] = IO::load(a.x, base, v);
+    }
+    // the batch's moments by two passes over its values, then one merge
+    float n = 0.f, s = 0.f;
+#pragma unroll
+    for (int k = 0; k < kGnSliceBatch; ++k) {
+      if (vb + (long long)k * kGnSliceThreads < v1) {
+        float f[VW];
+        IO::unpack(raw[k], f);
+#pragma unroll
+        for (int i = 0; i < VW; ++i) s += f[i];
+        n += (float)VW;
+      }
+    }
+    Moments b = {n, s * __builtin_amdgcn_rcpf(n), 0.f};
+#pragma unroll
+    for (int k = 0; k < kGnSliceBatch; ++k) {
+      if (vb + (long long)k * kGnSliceThreads < v1) {
+        float f[VW];
+        IO::unpack(raw[k], f);
+#pragma unroll
+        for (int i = 0; i < VW; ++i) b.m2 += (f[i] - b.mean) * (f[i] - b.mean);
+      }
+    }
+    merge(t, b);
+  }
+  const Moments m = block_merge<kGnSliceThreads>(t, lds);
+  if (threadIdx.x == 0) a.ws[blockIdx.x] = make_float2(m.mean, m.m2);
+}
+
+// Two-launch path, second launch: merge the group's slice moments, normalise
+// this slice.
+template <class E, bool kVec>
+__global__ __launch_bounds__(kGnSliceThreads) void gn_apply_kernel(const GnArgs a) {
+  using IO = GnIo<E, kVec>;
+  constexpr int VW = IO::VW;
+  __shared__ float2 coef;
+  const int tid = threadIdx.x;
+  const int grp = blockIdx.x / a.S, sl = blockIdx.x - grp * a.S;
+  const size_t base = (size_t)grp * a.L;
+  const long long lv = a.L / VW;
+  if (tid < 64) {
+    // lane j merges slices j, j + 64, ... in order, then the lanes merge
+    Moments g = {0.f, 0.f, 0.f};
+    for (int s = tid; s < a.S; s += 64) {
+      const float2 p = a.ws[(size_t)grp * a.S + s];
+      const long long s0 = (long long)s * a.slice_vec;
+      const long long s1 = s0 + a.slice_vec < lv ? s0 + a.slice_vec : lv;
+      const Moments m = {(float)((s1 - s0) * VW), p.x, p.y};
+      merge(g, m);
+    }
+    g = wave_merge(g);
+    if (tid == 0) coef = make_float2(g.mean, 1.f / __builtin_sqrtf(g.m2 / (float)a.L + a.eps));
   }
   __syncthreads();
   const float mean = coef.x, rstd = coef.y;
-
-  // phase 2: y = x a_c + b_c with a_c = rstd gamma_c, b_c = beta_c - mean a_c
-  const int gin = grp % a.G;  // group index within the sample
-  auto write_vector = [&](long long v, float* f) {
-    const int c = gin * a.Cg + (int)((v * VW) / a.HW);  // every element of a vector is in one channel
-    const float ga = a.gamma ? E::get(a.gamma, c) : 1.f;
-    const float be = a.beta ? E::get(a.beta, c) : 0.f;
-    const float sc = rstd * ga, sh = be - mean * sc;
+  const int gin = grp % a.G;
+  const long long v0 = (long long)sl * a.slice_vec;
+  const long long v1 = v0 + a.slice_vec < lv ? v0 + a.slice_vec : lv;
+  for (long long vb = v0 + tid; vb < v1; vb += (long long)kGnSliceThreads * kGnSliceBatch) {
+    typename IO::Raw raw[kGnSliceBatch];
 #pragma unroll
-    for (int i = 0; i < VW; ++i) f[i] = f[i] * sc + sh;
-    IO::store(a.y, base, v, f);
-  };
-  if constexpr (kResident) {
-#pragma unroll
-    for (int k = 0; k < kGnResidentVecs; ++k) {
-      const long long v = v0 + tid + (long long)k * kGnThreads;
-      if (v < v1) write_vector(v, xr[k]);
+    for (int k = 0; k < kGnSliceBatch; ++k) {
+      const long long v = vb + (long long)k * kGnSliceThreads;
+      if (v < v1) raw[k] = IO::load(a.x, base, v);
     }
-  } else {
-    for (long long v = v0 + tid; v < v1; v += kGnThreads) {
-      float f[VW];
-      IO::load(a.x, base, v, f);
-      write_vector(v, f);
+#pragma unroll
+    for (int k = 0; k < kGnSliceBatch; ++k) {
+      const long long v = vb + (long long)k * kGnSliceThreads;
+      if (v < v1) {
+        float f[VW];
+        IO::unpack(raw[k], f);
+        gn_write<E, kVec>(a, gin, base, v, f, mean, rstd);
+      }
     }
   }
 }
 
-// Workgroups a cooperative launch of `kern` can keep resident on the current
-// device (cached per device and kernel).
-int resident_capacity(const void* kern) {
-  static std::mutex mu;
-  static const void* keys[64];
-  static int devs[64], vals[64];
-  static int used = 0;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  {
-    std::lock_guard<std::mutex> g(mu);
-    for (int i = 0; i < used; ++i)
-      if (keys[i] == kern && devs[i] == dev) return vals[i];
+// The launch plan of one problem: fused (RV vectors per thread) or two
+// launches over S slices per group.
+struct GnPlan {
+  bool vec;
+  int rv;            // > 0: fused with rv vectors per thread
+  long long s;       // slices per group (two-launch path)
+  long long slice_vec;
+  size_t ws_bytes;   // workspace the plan needs
+};
+
+// ATTN_GN_PATH=split / fused forces a path (for measurements; fused only
+// where the group fits).
+int forced_path() {
+  const char* e = std::getenv("ATTN_GN_PATH");
+  if (!e) return 0;
+  if (!std::strcmp(e, "split")) return 1;
+  if (!std::strcmp(e, "fused")) return 2;
+  return 0;
+}
+
+template <class E>
+GnPlan gn_plan(const GroupNormProblem& p) {
+  GnPlan pl;
+  pl.vec = p.HW % E::VW == 0 && ((uintptr_t)p.x & 15u) == 0 && ((uintptr_t)p.y & 15u) == 0;
+  const int VW = pl.vec ? E::VW : 1;
+  const long long L = (long long)(p.C / p.G) * p.HW, lv = L / VW;
+  const long long ng = (long long)p.N * p.G;
+  pl.rv = 0;
+  pl.s = 1;
+  pl.slice_vec = lv;
+  pl.ws_bytes = 0;
+  // One launch when the group fits the registers and either the groups fill
+  // the chip (a workgroup of 1024 threads per group, one per CU or more) or
+  // they are small (two vectors per thread at most): a single workgroup
+  // moves only ~10-20 GB/s against HBM latency, so a few large groups go
+  // faster over many workgroups in two launches.
+  const int forced = forced_path();
+  int rv_fit = 0;
+  for (int rv = 1; rv <= kGnMaxRv && !rv_fit; rv *= 2)
+    if ((long long)rv * kGnFusedThreads >= lv) rv_fit = rv;
+  if (rv_fit && forced != 1 && (forced == 2 || ng >= kGnFusedMinGroups || rv_fit <= 2)) {
+    pl.rv = rv_fit;
+    return pl;
   }
-  int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kGnThreads, 0) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  const int cap = per_cu * cus;
-  std::lock_guard<std::mutex> g(mu);
-  if (used < 64) {
-    keys[used] = kern;
-    devs[used] = dev;
-    vals[used] = cap;
-    ++used;
-  }
-  return cap;
+  // two launches: about kGnSliceTarget workgroups, each slice at least one
+  // full batch of vectors per thread
+  const long long min_slice = (long long)kGnSliceThreads * kGnSliceBatch;
+  long long s = (kGnSliceTarget + ng - 1) / ng;
+  const long long most = (lv + min_slice - 1) / min_slice;
+  if (s > most) s = most;
+  if (s < 1) s = 1;
+  pl.slice_vec = (lv + s - 1) / s;
+  pl.s = (lv + pl.slice_vec - 1) / pl.slice_vec;  // every slice non-empty
+  pl.ws_bytes = (size_t)(ng * pl.s) * sizeof(float2);
+  return pl;
+}
+
+template <class E, bool kVec, int RV>
+void launch_fused(const GnArgs& a, long long ng, hipStream_t st) {
+  hipLaunchKernelGGL((gn_fused_kernel<E, kVec, RV>), dim3((unsigned)ng), dim3(kGnFusedThreads), 0, st, a);
 }
 
 template <class E, bool kVec>
-hipError_t launch_gn_t(const GroupNormProblem& p) {
-  constexpr int VW = kVec ? E::VW : 1;
+hipError_t launch_gn_t(const GroupNormProblem& p, const GnPlan& pl) {
   GnArgs a;
   a.x = p.x;
   a.gamma = p.gamma;
   a.beta = p.beta;
   a.y = p.y;
   a.ws = (float2*)p.workspace;
-  a.C = p.C;
   a.HW = p.HW;
   a.G = p.G;
   a.Cg = p.C / p.G;
   a.L = (long long)a.Cg * p.HW;
+  a.S = (int)pl.s;
+  a.slice_vec = pl.slice_vec;
   a.eps = p.eps;
-  const long long ng = (long long)p.N * p.G;  // groups
-  const long long lv = a.L / VW;               // vectors per group
-  const long long res_vecs = (long long)kGnThreads * kGnResidentVecs;
-  const long long s_res = (lv + res_vecs - 1) / res_vecs;  // slices for register residency
-
-  const void* k_split_res = (const void*)group_norm_kernel<E, true, true, kVec>;
-  const void* k_split_str = (const void*)group_norm_kernel<E, true, false, kVec>;
-  const long long max_grid = (long long)kGroupNormWorkspaceBytes / sizeof(float2);
-  // Slices per group.  Groups that fit one workgroup's registers get one
-  // workgroup (no barrier).  Larger groups are split -- when a workspace is
-  // given and the chip has room -- into at least s_res slices (x is then read
-  // once), as many as fill the resident workgroups, at most one vector per
-  // thread; groups too large for the resident grid are streamed (read twice).
-  long long s = 1;
-  bool resident = s_res == 1;
-  if (s_res > 1 && p.workspace && ng > 0) {
-    const int cap = resident_capacity(k_split_res);
-    const long long most = (lv + kGnThreads - 1) / kGnThreads;
-    if (s_res * ng <= cap && s_res * ng <= max_grid) {
-      const long long fill = cap / ng;
-      s = fill < most ? fill : most;
-      if (s < s_res) s = s_res;
-      resident = true;
-    } else {
-      const int cap_str = resident_capacity(k_split_str);
-      s = cap_str / ng;
-      if (s * ng > max_grid) s = max_grid / ng;
-      if (s < 1) s = 1;
-      resident = false;
+  const long long ng = (long long)p.N * p.G;
+  if (a.L >= 0x7fffffffLL) return hipErrorInvalidValue;
+  if (pl.rv > 0) {
+    if (ng > 0x7fffffffLL) return hipErrorInvalidValue;
+    switch (pl.rv) {
+      case 1: launch_fused<E, kVec, 1>(a, ng, p.stream); break;
+      case 2: launch_fused<E, kVec, 2>(a, ng, p.stream); break;
+      case 4: launch_fused<E, kVec, 4>(a, ng, p.stream); break;
+      case 8: launch_fused<E, kVec, 8>(a, ng, p.stream); break;
+      default: launch_fused<E, kVec, 16>(a, ng, p.stream); break;
     }
-  }
-  a.slice_vec = (lv + s - 1) / s;
-  s = (lv + a.slice_vec - 1) / a.slice_vec;  // every slice non-empty
-  a.S = (int)s;
-  const long long grid = ng * s;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-
-  if (s == 1) {
-    if (resident)
-      hipLaunchKernelGGL((group_norm_kernel<E, false, true, kVec>), dim3((unsigned)grid), dim3(kGnThreads), 0,
-                         p.stream, a);
-    else
-      hipLaunchKernelGGL((group_norm_kernel<E, false, false, kVec>), dim3((unsigned)grid), dim3(kGnThreads), 0,
-                         p.stream, a);
     return hipGetLastError();
   }
-  if (grid > max_grid) return hipErrorInvalidValue;
-  void* args[] = {&a};
-  return hipLaunchCooperativeKernel(resident ? k_split_res : k_split_str, dim3((unsigned)grid), dim3(kGnThreads),
-                                    args, 0, p.stream);
+  const long long grid = ng * pl.s;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gn_partial_kernel<E, kVec>), dim3((unsigned)grid), dim3(kGnSliceThreads), 0, p.stream, a);
+  hipLaunchKernelGGL((gn_apply_kernel<E, kVec>), dim3((unsigned)grid), dim3(kGnSliceThreads), 0, p.stream, a);
+  return hipGetLastError();
 }
 
 template <class E>
 hipError_t launch_gn_e(const GroupNormProblem& p) {
-  const bool vec = p.HW % E::VW == 0 && ((uintptr_t)p.x & 15u) == 0 && ((uintptr_t)p.y & 15u) == 0;
-  return vec ? launch_gn_t<E, true>(p) : launch_gn_t<E, false>(p);
+  const GnPlan pl = gn_plan<E>(p);
+  if (pl.ws_bytes > p.workspace_bytes || (pl.ws_bytes && !p.workspace)) return hipErrorInvalidValue;
+  return pl.vec ? launch_gn_t<E, true>(p, pl) : launch_gn_t<E, false>(p, pl);
+}
+
+template <class E>
+size_t gn_ws_e(const GroupNormProblem& p) {
+  return gn_plan<E>(p).ws_bytes;
 }
 
 // ---------------------------------------------------------------------------
@@ -484,6 +565,14 @@ hipError_t launch_group_norm(const GroupNormProblem& p) {
     case ATTN_F16: return launch_gn_e<EF16>(p);
     case ATTN_BF16: return launch_gn_e<EBF16>(p);
     default: return launch_gn_e<EF32>(p);
+  }
+}
+
+size_t group_norm_workspace(const GroupNormProblem& p) {
+  switch (p.dt) {
+    case ATTN_F16: return gn_ws_e<EF16>(p);
+    case ATTN_BF16: return gn_ws_e<EBF16>(p);
+    default: return gn_ws_e<EF32>(p);
   }
 }
 

@@ -219,6 +219,101 @@ def config_record(cfg, form: str, steps: int, cold: bool) -> dict:
     return rec
 
 
+# The UNet's other specialised kernels at SD 1.x 512x512 (batch 2) sizes, plus
+# the 1024x1024 decoder stress (groups of 327680 elements, streamed).
+GN_SHAPES = [(2, 320, 64 * 64), (2, 640, 64 * 64), (2, 960, 64 * 64), (2, 1280, 32 * 32),
+             (2, 1280, 16 * 16), (2, 2560, 8 * 8), (2, 640, 128 * 128), (8, 320, 64 * 64)]
+GEGLU_SHAPES = [(8192, 1280), (2048, 2560), (512, 5120), (128, 5120), (32768, 1280)]
+
+
+def _time_calls(fn, steps: int, warmup: int = 5):
+    """Median and min (ms) of `steps` calls, events around each call."""
+    import statistics
+    import torch
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for _ in range(warmup):
+        fn()
+    for e in ev:
+        e[0].record(stream)
+        fn()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    t = [e[0].elapsed_time(e[1]) for e in ev]
+    return statistics.median(t), min(t)
+
+
+def _time_graph(fn, calls: int = 20, reps: int = 7):
+    """Per-call GPU time (ms) of `calls` back-to-back calls captured in one
+    HIP graph (no host work between kernels), median over `reps` replays."""
+    import statistics
+    import torch
+    fn()  # warm-up outside the capture (workspaces, first-use setup)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t.append(e0.elapsed_time(e1) / calls)
+    return statistics.median(t)
+
+
+def unet_op_records(steps: int, dtype: str = "f16"):
+    """HBM throughput of attn_group_norm and attn_geglu: algorithmic bytes
+    (each input read once, each output written once) over the per-call time
+    of calls replayed back to back from a HIP graph (these kernels take a few
+    µs, less than the host needs to issue a call); the roofline fraction is
+    (bytes / 8 TB/s) / time.  median_us / min_us: events around single calls."""
+    import torch
+    import attention_attn_stats_amd as attn
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    es = {"f16": 2, "bf16": 2, "f32": 4}[dtype]
+    g = torch.Generator(device="cuda").manual_seed(0)
+    recs = []
+    for N, C, HW in GN_SHAPES:
+        x = torch.randn((N, C, HW), device="cuda", dtype=torch.float32, generator=g).to(tdt)
+        gamma = torch.ones(C, device="cuda", dtype=tdt)
+        beta = torch.zeros(C, device="cuda", dtype=tdt)
+        y = torch.empty_like(x)
+        by = 2 * x.numel() * es + 2 * C * es
+        for path in ("auto", "split", "fused"):
+            # 'split' / 'fused' force one form (ATTN_GN_PATH) for comparison
+            if path != "auto":
+                os.environ["ATTN_GN_PATH"] = path
+            fn = (lambda: attn.group_norm(x, 32, gamma, beta, eps=1e-5, out=y))
+            med, mn = _time_calls(fn, steps)
+            gt = _time_graph(fn)
+            os.environ.pop("ATTN_GN_PATH", None)
+            recs.append({"op": "group_norm", "shape": [N, C, HW], "groups": 32, "path": path, "dtype": dtype,
+                         "median_us": round(med * 1e3, 2), "min_us": round(mn * 1e3, 2),
+                         "graph_us": round(gt * 1e3, 2), "algorithmic_bytes": by,
+                         "GBps_graph": round(by / (gt * 1e-3) / 1e9, 1),
+                         "roofline_frac_graph": round(by / (HBM_GBS * 1e9) / (gt * 1e-3), 4)})
+    for rows, F in GEGLU_SHAPES:
+        h = torch.randn((rows, 2 * F), device="cuda", dtype=torch.float32, generator=g).to(tdt)
+        out = torch.empty((rows, F), device="cuda", dtype=tdt)
+        by = 3 * rows * F * es
+        fn = (lambda: attn.geglu(h, out=out))
+        med, mn = _time_calls(fn, steps)
+        gt = _time_graph(fn)
+        recs.append({"op": "geglu", "shape": [rows, F], "dtype": dtype,
+                     "median_us": round(med * 1e3, 2), "min_us": round(mn * 1e3, 2),
+                     "graph_us": round(gt * 1e3, 2), "algorithmic_bytes": by,
+                     "GBps_graph": round(by / (gt * 1e-3) / 1e9, 1),
+                     "roofline_frac_graph": round(by / (HBM_GBS * 1e9) / (gt * 1e-3), 4)})
+    return recs
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -270,6 +365,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--configs-out", default=None)
     ap.add_argument("--cold", action="store_true")
+    ap.add_argument("--unet-ops-out", default=None,
+                    help="also time group_norm and geglu at the UNet's sizes, JSONL there")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times (calibrates the "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -331,6 +428,12 @@ def main():
                     if var == "pf_scores" and c.dtype == "f32":
                         continue  # the stored-logit path runs on the matrix cores only
                     rec = config_record(c, var, max(20, args.steps // 4), args.cold)
+                    f.write(json.dumps(rec) + "\n")
+                    log(json.dumps(rec))
+    if args.unet_ops_out:
+        with open(args.unet_ops_out, "w") as f:
+            for dt in ("f16", "bf16"):
+                for rec in unet_op_records(max(20, args.steps // 4), dt):
                     f.write(json.dumps(rec) + "\n")
                     log(json.dumps(rec))
     if not args.no_cpu_baseline:

@@ -179,25 +179,33 @@ attn_status attn_scores_pv(const float* a, const float* ml, const void* v, void*
  * intermediate tensor, and GELU evaluated with the error function in one pass
  * together with the split and the multiplication around it. */
 
-/* Bytes of the optional group-normalisation workspace (device memory, 8-byte
- * aligned, contents need no initialisation; calls sharing one workspace must
- * not overlap in time). */
-#define ATTN_GROUP_NORM_WORKSPACE_BYTES 131072
-
 /* Group normalisation of x [N][C][HW] (NCHW, spatial dims flattened) with G
  * groups of C/G consecutive channels: per (n, g) the mean and the biased
  * variance over the group's (C/G)*HW elements, then
  * y = (x - mean) / sqrt(var + eps) * gamma[c] + beta[c].  Statistics in
- * float32 (pairwise merged moments, never sums of squares).  gamma, beta: [C]
- * in dt, or NULL for 1 and 0.  y [N][C][HW] in dt, written; y may equal x.
- * One launch.  With a workspace, large groups are split over several
- * workgroups that exchange their moments at a grid barrier (a cooperative
- * launch); with NULL, each group is one workgroup.  Requirements: sizes >= 1,
- * C a multiple of G, eps finite and >= 0, pointers aligned to the element
- * size, N*C*HW < 2^40.  Violations return ATTN_ERR_INVALID_ARG before anything
- * is launched. */
+ * float32 (pairwise merged moments, never sums of squares), deterministic.
+ * gamma, beta: [C] in dt, or NULL for 1 and 0.  y [N][C][HW] in dt, written;
+ * y may equal x.  When a group fits one workgroup's registers (up to 131072
+ * fp16/bf16 or 65536 fp32 elements when x, y are 16-byte aligned and HW*size
+ * is a multiple of 16 bytes; 16384 elements otherwise) and the groups fill
+ * the chip or are small, it is normalised in one launch, x read once, with
+ * no intermediate tensor.  Otherwise two launches over slices of the groups
+ * run, with a workspace of attn_group_norm_workspace_size() bytes (device
+ * memory, 8-byte aligned, no initialisation; calls sharing one workspace must
+ * not overlap in time); workspace may be NULL when that size is 0.
+ * Requirements: sizes >= 1, C a multiple of G, eps finite and >= 0, pointers
+ * aligned to the element size, (C/G)*HW < 2^31, N*C*HW < 2^40; else
+ * ATTN_ERR_INVALID_ARG before anything is launched (also for a missing or
+ * short workspace). */
 attn_status attn_group_norm(const void* x, const void* gamma, const void* beta, void* y, void* workspace,
-                            int N, int C, int HW, int G, float eps, attn_dtype dt, void* stream);
+                            size_t workspace_bytes, int N, int C, int HW, int G, float eps, attn_dtype dt,
+                            void* stream);
+
+/* Workspace bytes attn_group_norm needs for this problem (0: none).  The
+ * alignment of x and y enters the plan, so pass the pointers that will be
+ * used.  Returns 0 for invalid arguments as well. */
+size_t attn_group_norm_workspace_size(const void* x, const void* y, int N, int C, int HW, int G,
+                                      attn_dtype dt);
 
 /* GELU-gated product: h [rows][2F] -> out [rows][F],
  * out[r][j] = h[r][j] * gelu(h[r][F + j]), gelu(g) = g Phi(g) =

@@ -153,22 +153,35 @@ def test_strided_stats_checks_only_q_and_k(lib):
 
 def test_group_norm_and_geglu_validation(lib):
     f = _lib.F16
-    # attn_group_norm(x, gamma, beta, y, workspace, N, C, HW, G, eps, dt, stream)
-    gn = lib.attn_group_norm
-    assert gn(None, None, None, P, P, 2, 32, 64, 32, 1e-5, f, None) == _lib.ERR_INVALID_ARG
-    assert gn(P, None, None, None, P, 2, 32, 64, 32, 1e-5, f, None) == _lib.ERR_INVALID_ARG
-    assert gn(P, None, None, P, P, 2, 30, 64, 4, 1e-5, f, None) == _lib.ERR_INVALID_ARG      # C % G
-    assert gn(P, None, None, P, P, 0, 32, 64, 32, 1e-5, f, None) == _lib.ERR_INVALID_ARG     # N
-    assert gn(P, None, None, P, P, 2, 32, 0, 32, 1e-5, f, None) == _lib.ERR_INVALID_ARG      # HW
-    assert gn(P, None, None, P, P, 2, 32, 64, 0, 1e-5, f, None) == _lib.ERR_INVALID_ARG      # G
-    assert gn(P, None, None, P, P, 2, 32, 64, 32, -1.0, f, None) == _lib.ERR_INVALID_ARG     # eps
-    assert gn(P, None, None, P, P, 2, 32, 64, 32, float("nan"), f, None) == _lib.ERR_INVALID_ARG
-    assert gn(P + 1, None, None, P, P, 2, 32, 64, 32, 1e-5, f, None) == _lib.ERR_INVALID_ARG  # x alignment
-    assert gn(P, P + 1, None, P, P, 2, 32, 64, 32, 1e-5, f, None) == _lib.ERR_INVALID_ARG     # gamma alignment
-    assert gn(P, None, None, P, P + 4, 2, 32, 64, 32, 1e-5, f, None) == _lib.ERR_INVALID_ARG  # workspace alignment
-    assert gn(P + 2, None, None, P, P, 2, 32, 64, 32, 1e-5, _lib.F32, None) == _lib.ERR_INVALID_ARG
-    assert gn(P, None, None, P, P, 1 << 16, 1 << 12, 1 << 12, 32, 1e-5, f, None) == _lib.ERR_INVALID_ARG
-    assert gn(P, None, None, P, P, 2, 32, 64, 32, 1e-5, 9, None) == _lib.ERR_UNSUPPORTED
+    # attn_group_norm(x, gamma, beta, y, workspace, workspace_bytes, N, C, HW, G, eps, dt, stream)
+    def gn(x, ga, be, y, ws, N, C, HW, G, eps, dt):
+        return lib.attn_group_norm(x, ga, be, y, ws, 1 << 20, N, C, HW, G, eps, dt, None)
+    assert gn(None, None, None, P, P, 2, 32, 64, 32, 1e-5, f) == _lib.ERR_INVALID_ARG
+    assert gn(P, None, None, None, P, 2, 32, 64, 32, 1e-5, f) == _lib.ERR_INVALID_ARG
+    assert gn(P, None, None, P, P, 2, 30, 64, 4, 1e-5, f) == _lib.ERR_INVALID_ARG      # C % G
+    assert gn(P, None, None, P, P, 0, 32, 64, 32, 1e-5, f) == _lib.ERR_INVALID_ARG     # N
+    assert gn(P, None, None, P, P, 2, 32, 0, 32, 1e-5, f) == _lib.ERR_INVALID_ARG      # HW
+    assert gn(P, None, None, P, P, 2, 32, 64, 0, 1e-5, f) == _lib.ERR_INVALID_ARG      # G
+    assert gn(P, None, None, P, P, 2, 32, 64, 32, -1.0, f) == _lib.ERR_INVALID_ARG     # eps
+    assert gn(P, None, None, P, P, 2, 32, 64, 32, float("nan"), f) == _lib.ERR_INVALID_ARG
+    assert gn(P + 1, None, None, P, P, 2, 32, 64, 32, 1e-5, f) == _lib.ERR_INVALID_ARG  # x alignment
+    assert gn(P, P + 1, None, P, P, 2, 32, 64, 32, 1e-5, f) == _lib.ERR_INVALID_ARG     # gamma alignment
+    assert gn(P, None, None, P, P + 4, 2, 32, 64, 32, 1e-5, f) == _lib.ERR_INVALID_ARG  # workspace alignment
+    assert gn(P + 2, None, None, P, P, 2, 32, 64, 32, 1e-5, _lib.F32) == _lib.ERR_INVALID_ARG
+    assert gn(P, None, None, P, P, 1 << 16, 1 << 12, 1 << 12, 32, 1e-5, f) == _lib.ERR_INVALID_ARG
+    assert gn(P, None, None, P, P, 2, 32, 64, 32, 1e-5, 9) == _lib.ERR_UNSUPPORTED
+    # workspace: none for groups that fit one workgroup, some for larger ones,
+    # and a missing or short one is refused before launch
+    ws = lib.attn_group_norm_workspace_size
+    assert ws(P, P, 2, 2560, 8 * 8, 32, f) == 0       # small groups: one launch
+    assert ws(P, P, 8, 320, 64 * 64, 32, f) == 0      # 256 groups fill the chip: one launch
+    need = ws(P, P, 2, 640, 128 * 128, 32, f)
+    assert need > 0 and need % 8 == 0
+    assert ws(P, P, 2, 30, 64, 4, f) == 0  # invalid sizes
+    assert lib.attn_group_norm(P, None, None, P, None, 0, 2, 640, 128 * 128, 32, 1e-5, f, None) == \
+        _lib.ERR_INVALID_ARG
+    assert lib.attn_group_norm(P, None, None, P, P, need - 8, 2, 640, 128 * 128, 32, 1e-5, f, None) == \
+        _lib.ERR_INVALID_ARG
     # attn_geglu(h, out, rows, F, dt, stream)
     ge = lib.attn_geglu
     assert ge(None, P, 4, 8, f, None) == _lib.ERR_INVALID_ARG

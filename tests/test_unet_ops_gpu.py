@@ -13,9 +13,9 @@ element by element, within bounds derived from the arithmetic:
   1e-7 g^2).
 
 Shapes: the SD 1.x UNet's normalisation and feed-forward sizes at 512x512
-(batch 2), every launch form of the group normalisation (one workgroup per
-group; groups split over workgroups with a grid barrier, x held in registers;
-split and streamed; streamed without a workspace), ragged and unaligned
+(batch 2), both launch forms of the group normalisation (one launch with the
+group in one workgroup's registers, at every register depth; two launches over
+slices for larger groups, also forced on small ones), ragged and unaligned
 sizes (element-wise paths), in-place use, and activations with a large common
 offset (mean 100, sigma 1), where a sum-of-squares variance would fail."""
 import numpy as np
@@ -50,7 +50,7 @@ def _host(t) -> np.ndarray:
 
 
 # ---- group normalisation -----------------------------------------------
-def _gn_case(N, C, HW, G, dtype, seed, mean=0.0, sigma=1.0, affine=True, split=True, inplace=False,
+def _gn_case(N, C, HW, G, dtype, seed, mean=0.0, sigma=1.0, affine=True, inplace=False,
              offset_elems=0, eps=1e-5):
     import torch
     import attention_attn_stats_amd as attn
@@ -72,7 +72,7 @@ def _gn_case(N, C, HW, G, dtype, seed, mean=0.0, sigma=1.0, affine=True, split=T
         tg = tb = gw = bw = None
     y_ref, m_ref, r_ref = ops.group_norm(xw, G, gw, bw, eps)
     out = tx if inplace else None
-    y = attn.group_norm(tx, G, tg, tb, eps=eps, out=out, split=split)
+    y = attn.group_norm(tx, G, tg, tb, eps=eps, out=out)
     torch.cuda.synchronize()
     yh = _host(y)
     ga = np.abs(gw)[None, :, None] if affine else 1.0
@@ -102,11 +102,41 @@ def test_group_norm_sd_shapes(C, HW, dtype):
     print(f"gn C{C} HW{HW} {dtype} err/bound {r:.3f}", flush=True)
 
 
-@pytest.mark.parametrize("split", [True, False])
-def test_group_norm_large_groups_streamed(split):
+def test_group_norm_large_groups_two_launches():
     # 1024x1024 image, decoder input: 640 channels at 128x128: groups of
-    # 327680 elements; streamed (x read twice), split or one workgroup per group
-    _gn_case(2, 640, 128 * 128, 32, "f16", seed=7, split=split)
+    # 327680 elements, beyond one workgroup's registers
+    import attention_attn_stats_amd as attn
+    from attention_attn_stats_amd import _lib
+    assert _lib.load().attn_group_norm_workspace_size(1 << 20, 1 << 20, 2, 640, 128 * 128, 32, _lib.F16) > 0
+    _gn_case(2, 640, 128 * 128, 32, "f16", seed=7)
+    _gn_case(1, 64, 40000, 2, "f32", seed=8)          # f32: 65536-element register limit
+    _gn_case(1, 32, 20001, 1, "bf16", seed=9)         # element-wise path beyond 16384 elements
+    del attn
+
+
+@pytest.mark.parametrize("C,HW", [(320, 4096), (64, 100), (1280, 64)], ids=lambda v: str(v))
+def test_group_norm_two_launch_path_forced(C, HW, monkeypatch):
+    # the two-launch form on groups that would fit one workgroup, through the
+    # same entry point (the plan reads ATTN_GN_PATH at every call)
+    monkeypatch.setenv("ATTN_GN_PATH", "split")
+    for dtype in ("f16", "f32"):
+        _gn_case(2, C, HW, 32, dtype, seed=C + HW + 1)
+
+
+@pytest.mark.parametrize("rv_elems", [1000, 9000, 20000, 40000, 70000, 130000])
+def test_group_norm_every_register_depth(rv_elems, monkeypatch):
+    # groups of about rv_elems fp16 elements in one launch: 1, 2, 4, 8, 16
+    # vectors per thread (forced: so few groups would otherwise take two)
+    monkeypatch.setenv("ATTN_GN_PATH", "fused")
+    _gn_case(2, 2, rv_elems // 8 * 8, 2, "f16", seed=rv_elems)
+    _gn_case(1, 4, rv_elems // 16 * 4, 2, "f32", seed=rv_elems + 1)
+
+
+def test_group_norm_many_groups_one_launch():
+    # batch 8: 256 groups fill the chip in one launch
+    from attention_attn_stats_amd import _lib
+    assert _lib.load().attn_group_norm_workspace_size(1 << 20, 1 << 20, 8, 320, 64 * 64, 32, _lib.F16) == 0
+    _gn_case(8, 320, 64 * 64, 32, "f16", seed=31)
 
 
 def test_group_norm_large_common_offset():
@@ -135,16 +165,18 @@ def test_group_norm_forms_agree_and_options():
     _gn_case(2, 320, 64 * 64, 32, "f32", seed=26, eps=0.0)
 
 
-def test_group_norm_split_is_deterministic():
+def test_group_norm_is_deterministic_and_forms_agree(monkeypatch):
     import torch
     import attention_attn_stats_amd as attn
     x = torch.randn(2, 320, 64, 64, device="cuda", dtype=torch.float16)
     y0 = attn.group_norm(x, 32)
     for _ in range(3):
         assert torch.equal(attn.group_norm(x, 32), y0)
-    # one workgroup per group merges the moments in another order: the two
-    # agree to one rounding of the fp16 output
-    y1 = attn.group_norm(x, 32, split=False)
+    # the two-launch form merges the moments in another order: the two agree
+    # to one rounding of the fp16 output
+    monkeypatch.setenv("ATTN_GN_PATH", "split")
+    y1 = attn.group_norm(x, 32)
+    assert torch.equal(attn.group_norm(x, 32), y1)
     d = (y1.float() - y0.float()).abs()
     assert bool((d <= 2.0 ** -10 * y0.float().abs() + 2.0 ** -24).all()), d.max().item()
 
