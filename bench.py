@@ -314,6 +314,21 @@ def unet_op_records(steps: int, dtype: str = "f16"):
     return recs
 
 
+def oracle_single_thread(cfg) -> dict:
+    """The float64 oracle on one host thread over the whole config (the small
+    configs only: a few seconds each), as a per-config CPU reference."""
+    import oracle
+    from attention_attn_stats_amd import synth
+    q, k, v = (synth.widen(x, cfg.dtype) for x in cfg.inputs())
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, cfg.scale, nthreads=1)
+    t = time.perf_counter() - t0
+    return {"oracle_1thread_s": round(t, 4), "oracle_1thread_tflops": round(cfg.flops / t / 1e12, 6)}
+
+
+SMALL_FOR_ORACLE = ("tiny", "tiny8", "sd512_cross", "level2_self", "level3_self", "level4_self")
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -424,10 +439,12 @@ def main():
     if args.configs_out:
         with open(args.configs_out, "w") as f:
             for name, c in CONFIGS.items():
+                cpu = oracle_single_thread(c) if name in SMALL_FOR_ORACLE and not args.no_cpu_baseline else {}
                 for var in args.forms.split(","):
                     if var == "pf_scores" and c.dtype == "f32":
                         continue  # the stored-logit path runs on the matrix cores only
                     rec = config_record(c, var, max(20, args.steps // 4), args.cold)
+                    rec.update(cpu)
                     f.write(json.dumps(rec) + "\n")
                     log(json.dumps(rec))
     if args.unet_ops_out:
