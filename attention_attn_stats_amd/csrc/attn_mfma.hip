@@ -97,8 +97,8 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 
 // Raw buffer resource over `bytes` bytes at p (stride 0): loads at offsets
 // at or past `bytes` return zero without touching memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, static_cast<int>(bytes), 0x00020000);
 }
 __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rs, int voff) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
@@ -348,8 +348,9 @@ __global__ __launch_bounds__(Shape<D>::T) void fwd_kernel(const uint16_t* __rest
   auto gload = [&](int it) {
     const int key0 = (2 * it + halfu) * BN;
     // the resources end after the last key's d elements
-    const int kbytes = Nk > key0 ? ((Nk - key0 - 1) * krs_ + D) * 2 : 0;
-    const int vbytes = Nk > key0 ? ((Nk - key0 - 1) * vrs_ + D) * 2 : 0;
+    // up to 2^32 - 2 bytes (a head holds fewer than 2^31 elements): unsigned
+    const unsigned kbytes = Nk > key0 ? ((unsigned)(Nk - key0 - 1) * (unsigned)krs_ + D) * 2u : 0u;
+    const unsigned vbytes = Nk > key0 ? ((unsigned)(Nk - key0 - 1) * (unsigned)vrs_ + D) * 2u : 0u;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(kh + (size_t)key0 * krs_, kbytes);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc((kStats ? kh : vh) + (size_t)key0 * vrs_, kStats ? 0 : vbytes);
 #pragma unroll
