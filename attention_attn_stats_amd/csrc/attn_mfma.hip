@@ -182,7 +182,7 @@ __device__ __forceinline__ int vrow(int k) { return k ^ (((k >> 4) & 1) << 2); }
 
 constexpr int kQ = 32;              // queries per wave
 
-template <int D>
+template <int D, int MODE>
 struct Shape {
   static constexpr int KS = (D + 15) / 16;      // K=16 steps of Q K^T
   static constexpr int MT = (D + 15) / 16;      // 16-row tiles of O^T
@@ -194,8 +194,14 @@ struct Shape {
   // vrow permutation); d = 40 needs padding columns 40..47 in both.
   static constexpr int PK = D == 40 ? 56 : D + 8;
   static constexpr int PV = D == 40 ? 48 : (D == 80 ? 80 : D + 16);
-  static constexpr int BN = D == 40 ? 64 : 32;   // keys per block
-  static constexpr int QG = D == 40 ? 8 : 4;     // query groups per workgroup
+  // keys per block: 64 at d = 40, and at d = 80 for the single pass (measured
+  // 7-13 % faster there; the two-pass form stays at 32, where 64 was slower at
+  // N >= 4096); 32 otherwise
+  static constexpr bool kFlashLike = MODE == kModeFlash || MODE == kModeFlashML;
+  static constexpr int BN = (D == 40 || (D == 80 && kFlashLike)) ? 64 : 32;
+  // query groups per workgroup: d = 160 takes 2 (half the workgroup, twice
+  // the workgroups for the small sequences of the UNet's deep levels)
+  static constexpr int QG = D == 40 ? 8 : (D == 160 ? 2 : 4);
   static constexpr int W = 2 * QG;               // waves per workgroup (x 2 key halves)
   static constexpr int T = 64 * W;               // threads per workgroup
   static constexpr int HT = 64 * QG;             // threads per key half
@@ -208,19 +214,16 @@ struct Shape {
 };
 
 template <class TR, int D, int MODE>
-__global__ __launch_bounds__(Shape<D>::T) void fwd_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__((Shape<D, MODE>::T)) void fwd_kernel(const uint16_t* __restrict__ q,
                                                  const uint16_t* __restrict__ k,
                                                  const uint16_t* __restrict__ v,
                                                  uint16_t* __restrict__ out,
                                                  float* __restrict__ ml, const float* __restrict__ a,
                                                  const Layout lay, int Nq, int Nk, int qtiles, int nwg,
                                                  float scale) {
-  using S = Shape<D>;
+  using S = Shape<D, MODE>;
   constexpr int KS = S::KS, MT = S::MT, PK = S::PK, PV = S::PV, NBUF = S::NBUF;
   constexpr int BN = S::BN, NT = S::NT, kQG = S::QG, kHT = S::HT, kQWG = S::QWG;
-  // Fold scale and max subtraction into the MFMA (fp16, d with a spare dim).
-  // Not when (m, l) is reported: the pre-scaled Q perturbs the scores by up to
-  // a few 1e-4 of their exp2 value, too close to the 1e-3 bound on l.
   constexpr bool kStats = MODE == kModeStats;
   constexpr bool kFromA = MODE == kModePVScores;             // logits read from A (float32)
   constexpr bool kPVLike = MODE == kModePV || kFromA;        // (m, l) given, O only
@@ -644,11 +647,11 @@ __global__ __launch_bounds__(Shape<D>::T) void fwd_kernel(const uint16_t* __rest
 
 template <class TR, int D, int MODE>
 hipError_t launch_fwd_t(const Problem& p) {
-  constexpr int kQWG = Shape<D>::QWG;
+  constexpr int kQWG = Shape<D, MODE>::QWG;
   const int qtiles = (p.Nq + kQWG - 1) / kQWG;
   const long long nwg = (long long)p.BH * qtiles;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_kernel<TR, D, MODE>), dim3((unsigned)nwg), dim3(Shape<D>::T), 0, p.stream,
+  hipLaunchKernelGGL((fwd_kernel<TR, D, MODE>), dim3((unsigned)nwg), dim3((Shape<D, MODE>::T)), 0, p.stream,
                      (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v, (uint16_t*)p.out,
                      p.ml, p.a, p.lay, p.Nq, p.Nk, qtiles, (int)nwg, p.scale);
   return hipGetLastError();
