@@ -182,7 +182,7 @@ __device__ __forceinline__ int vrow(int k) { return k ^ (((k >> 4) & 1) << 2); }
 
 constexpr int kQ = 32;              // queries per wave
 
-template <int D, int MODE>
+template <int D, int MODE, bool kHalfQ = false>
 struct Shape {
   static constexpr int KS = (D + 15) / 16;      // K=16 steps of Q K^T
   static constexpr int MT = (D + 15) / 16;      // 16-row tiles of O^T
@@ -200,8 +200,10 @@ struct Shape {
   static constexpr bool kFlashLike = MODE == kModeFlash || MODE == kModeFlashML;
   static constexpr int BN = (D == 40 || (D == 80 && kFlashLike)) ? 64 : 32;
   // query groups per workgroup: d = 160 takes 2 (half the workgroup, twice
-  // the workgroups for the small sequences of the UNet's deep levels)
-  static constexpr int QG = D == 40 ? 8 : (D == 160 ? 2 : 4);
+  // the workgroups for the small sequences of the UNet's deep levels);
+  // kHalfQ halves it again for problems with fewer workgroups than CUs
+  static constexpr int QG0 = D == 40 ? 8 : (D == 160 ? 2 : 4);
+  static constexpr int QG = kHalfQ && QG0 > 1 ? QG0 / 2 : QG0;
   static constexpr int W = 2 * QG;               // waves per workgroup (x 2 key halves)
   static constexpr int T = 64 * W;               // threads per workgroup
   static constexpr int HT = 64 * QG;             // threads per key half
@@ -213,15 +215,15 @@ struct Shape {
   static_assert(D % 8 == 0 && D >= 16, "head dim must be a multiple of 8");
 };
 
-template <class TR, int D, int MODE>
-__global__ __launch_bounds__((Shape<D, MODE>::T)) void fwd_kernel(const uint16_t* __restrict__ q,
+template <class TR, int D, int MODE, bool kHalfQ>
+__global__ __launch_bounds__((Shape<D, MODE, kHalfQ>::T)) void fwd_kernel(const uint16_t* __restrict__ q,
                                                  const uint16_t* __restrict__ k,
                                                  const uint16_t* __restrict__ v,
                                                  uint16_t* __restrict__ out,
                                                  float* __restrict__ ml, const float* __restrict__ a,
                                                  const Layout lay, int Nq, int Nk, int qtiles, int nwg,
                                                  float scale) {
-  using S = Shape<D, MODE>;
+  using S = Shape<D, MODE, kHalfQ>;
   constexpr int KS = S::KS, MT = S::MT, PK = S::PK, PV = S::PV, NBUF = S::NBUF;
   constexpr int BN = S::BN, NT = S::NT, kQG = S::QG, kHT = S::HT, kQWG = S::QWG;
   constexpr bool kStats = MODE == kModeStats;
@@ -645,16 +647,42 @@ __global__ __launch_bounds__((Shape<D, MODE>::T)) void fwd_kernel(const uint16_t
   }
 }
 
-template <class TR, int D, int MODE>
-hipError_t launch_fwd_t(const Problem& p) {
-  constexpr int kQWG = Shape<D, MODE>::QWG;
-  const int qtiles = (p.Nq + kQWG - 1) / kQWG;
-  const long long nwg = (long long)p.BH * qtiles;
-  if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_kernel<TR, D, MODE>), dim3((unsigned)nwg), dim3((Shape<D, MODE>::T)), 0, p.stream,
-                     (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v, (uint16_t*)p.out,
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int counts[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (counts[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    counts[dev] = n;  // the same value from every thread: a benign race
+  }
+  return counts[dev];
+}
+
+template <class TR, int D, int MODE, bool kHalfQ>
+hipError_t launch_fwd_q(const Problem& p, int qtiles, long long nwg) {
+  hipLaunchKernelGGL((fwd_kernel<TR, D, MODE, kHalfQ>), dim3((unsigned)nwg), dim3((Shape<D, MODE, kHalfQ>::T)), 0,
+                     p.stream, (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v, (uint16_t*)p.out,
                      p.ml, p.a, p.lay, p.Nq, p.Nk, qtiles, (int)nwg, p.scale);
   return hipGetLastError();
+}
+
+// Workgroups of the default shape when they fill the chip; otherwise half
+// the query groups per workgroup and twice the workgroups (every wave does
+// the same work either way, so the results are identical).
+template <class TR, int D, int MODE>
+hipError_t launch_fwd_t(const Problem& p) {
+  using S = Shape<D, MODE, false>;
+  using H = Shape<D, MODE, true>;
+  const int qtiles = (p.Nq + S::QWG - 1) / S::QWG;
+  const long long nwg = (long long)p.BH * qtiles;
+  if (H::QG < S::QG && nwg < cu_count()) {
+    const int qt2 = (p.Nq + H::QWG - 1) / H::QWG;
+    return launch_fwd_q<TR, D, MODE, true>(p, qt2, (long long)p.BH * qt2);
+  }
+  if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
+  return launch_fwd_q<TR, D, MODE, false>(p, qtiles, nwg);
 }
 
 template <template <class, int> class L, class TR>

@@ -174,3 +174,30 @@ def test_bitwise_repeatable_and_stream_independent(name):
         for a, b in zip(got[f], ref[f]):
             assert torch.equal(a, b), f"{name}/{f}: side-stream result differs"
     assert torch.equal(got_auto, ref["auto"][0])
+
+
+@pytest.mark.parametrize("d,qwg", [(40, 256), (80, 128), (160, 64)])
+@pytest.mark.parametrize("form", FORMS)
+def test_workgroup_shape_does_not_change_results(d, qwg, form):
+    """A problem with fewer workgroups than CUs runs with half the query groups
+    per workgroup; each wave does the same work either way.  Row i depends on
+    q_i, K and V only, so the first rows of a problem one workgroup short of
+    filling the chip (halved shape) equal those of one that fills it (default
+    shape) bit for bit."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    dtype, Nk = "f16", 300
+    n_big = cus * qwg
+    n_small = (cus - 1) * qwg
+    q = synth.tensor(71 + d, (1, 1, n_big, d), dtype)
+    k = synth.tensor(72 + d, (1, 1, Nk, d), dtype)
+    v = synth.tensor(73 + d, (1, 1, Nk, d), dtype)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    tk, tv = to_device(k, dtype), to_device(v, dtype)
+    o_big, ml_big = _forward(to_device(q, dtype), tk, tv, form, scale)
+    o_small, ml_small = _forward(to_device(np.ascontiguousarray(q[:, :, :n_small]), dtype), tk, tv, form, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o_small, o_big[:, :, :n_small]), f"d={d} {form}: O differs between workgroup shapes"
+    assert torch.equal(ml_small, ml_big[:, :, :n_small])
+    o_ref, ml_ref = reference(q[:, :, :512], k, v, dtype, scale)
+    assert_close_o(from_device(o_small)[:, :, :512], o_ref, dtype, f"d={d} {form} halved shape")
