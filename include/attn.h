@@ -19,6 +19,11 @@
  *    the choice is made by timing both on the device (attn_select, and
  *    attn_forward with ATTN_AUTO).
  *
+ * Further below: the partially fused form over a stored logit matrix
+ * (attn_scores*, the write-up's literal data flow), the four operations on
+ * strided tensors (attn_*_strided), and the UNet's two other specialised
+ * kernels of the same write-up (attn_group_norm, attn_geglu).
+ *
  * Definitions used throughout (the pages name the two per-row quantities
  * only as "L and S"; they are read here as the row maximum and the row sum
  * of exponentials relative to it, in natural-log units, scale included):
@@ -27,7 +32,7 @@
  *     l_i  = sum_j exp(a_ij - m_i)          (so 1 <= l_i <= Nk)
  *     O_ic = sum_j exp(a_ij - m_i) v_jc / l_i
  *
- * Layouts (all dense, row-major, no strides):
+ * Layouts of the functions without "_strided" (dense, row-major):
  *     q, out : [B][H][Nq][d]   element type given by `dt`
  *     k, v   : [B][H][Nk][d]   element type given by `dt`
  *     ml     : [B][H][Nq][2]   float32, ml[..][0] = m, ml[..][1] = l
