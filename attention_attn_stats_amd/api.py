@@ -222,7 +222,7 @@ def _gn_workspace(device, nbytes: int) -> torch.Tensor:
     key = (device, torch.cuda.current_stream(device).cuda_stream)
     ws = _GN_WS.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)  # zero-filled before first use
         _GN_WS[key] = ws
     return ws
 

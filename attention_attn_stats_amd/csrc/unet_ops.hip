@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 #include <type_traits>
@@ -85,15 +86,20 @@ struct EF32 {
 // M2 + M2' + d^2 n n'/(n + n')), d = m' - m, in a fixed order, so results are
 // deterministic and never rely on E[x^2] - E[x]^2.
 //
-// One launch (gn_fused_kernel) whenever a group fits one workgroup's
-// registers: 1024 threads hold up to 16 vectors each (131072 fp16/bf16 or
-// 65536 fp32 elements), every load of the group is issued before the first
-// is used, the moments are merged across the workgroup, and the group is
-// written from registers -- x read once, y written once, no intermediate
-// tensor.  Larger groups take two launches over S slices per group: the
-// first writes each slice's moments to a small workspace, the second merges
-// its group's S moments (in slice order, identically in every workgroup) and
-// normalises its slice, reading x a second time.
+// Three forms, all reading x from HBM once except the last:
+//  - gn_fused_kernel: one 1024-thread workgroup per group holds the group in
+//    registers (up to 16 vectors per thread: 131072 fp16/bf16 or 65536 fp32
+//    elements), issues every load before using any, merges the moments
+//    across the workgroup and writes the group from registers.  Used when
+//    the groups fill the chip or are small.
+//  - gn_coop_kernel: S workgroups per group, each holding its slice in
+//    registers, exchange slice moments through a small workspace at a
+//    per-group arrival counter (bounded wait, see there) -- one launch for
+//    the few large groups of a batch-2 UNet.
+//  - gn_partial_kernel + gn_apply_kernel: two launches over S slices (the
+//    first writes each slice's moments, the second merges its group's
+//    moments in slice order and normalises its slice, reading x again), for
+//    groups beyond what the resident workgroups can hold.
 // ---------------------------------------------------------------------------
 constexpr int kGnFusedThreads = 1024, kGnMaxRv = 16;
 constexpr int kGnSliceThreads = 256, kGnSliceBatch = 4;  // vectors in flight per thread when streaming
@@ -105,7 +111,12 @@ struct GnArgs {
   const void* gamma;  // [C] or null
   const void* beta;   // [C] or null
   void* y;
-  float2* ws;          // [groups][S] (mean, M2) per slice (two-launch path)
+  // [groups][S][2] slice moments (split forms) as 64-bit words: the float
+  // bits of the mean (word 0) or of M2 (word 1) in the low half, the call's
+  // epoch in the high half
+  unsigned long long* ws;
+  unsigned epoch;      // nonzero, different for every call on a workspace
+  int spin_limit;      // polls before a workgroup stops waiting for its group
   long long L;         // elements per group
   long long slice_vec; // vectors per slice (the last slice of a group may be shorter)
   int HW, G, Cg, S;
@@ -115,6 +126,11 @@ struct GnArgs {
 struct Moments {
   float n, mean, m2;
 };
+
+__device__ __forceinline__ unsigned long long tag(float v, unsigned epoch) {
+  return ((unsigned long long)epoch << 32) | __float_as_uint(v);
+}
+__device__ __forceinline__ float untag(unsigned long long w) { return __uint_as_float((unsigned)w); }
 
 __device__ __forceinline__ void merge(Moments& a, const Moments& b) {
   if (b.n == 0.f) return;
@@ -154,6 +170,7 @@ __device__ __forceinline__ Moments wave_merge(Moments t) {
 template <int NT>
 __device__ Moments block_merge(Moments t, Moments* lds) {
   t = wave_merge(t);
+  __syncthreads();  // a previous call's readers are done with lds
   if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = t;
   __syncthreads();
   Moments r = lds[0];
@@ -299,7 +316,10 @@ __global__ __launch_bounds__(kGnSliceThreads) void gn_partial_kernel(const GnArg
     merge(t, b);
   }
   const Moments m = block_merge<kGnSliceThreads>(t, lds);
-  if (threadIdx.x == 0) a.ws[blockIdx.x] = make_float2(m.mean, m.m2);
+  if (threadIdx.x == 0) {
+    a.ws[2 * (size_t)blockIdx.x] = tag(m.mean, a.epoch);
+    a.ws[2 * (size_t)blockIdx.x + 1] = tag(m.m2, a.epoch);
+  }
 }
 
 // Two-launch path, second launch: merge the group's slice moments, normalise
@@ -317,7 +337,8 @@ __global__ __launch_bounds__(kGnSliceThreads) void gn_apply_kernel(const GnArgs 
     // lane j merges slices j, j + 64, ... in order, then the lanes merge
     Moments g = {0.f, 0.f, 0.f};
     for (int s = tid; s < a.S; s += 64) {
-      const float2 p = a.ws[(size_t)grp * a.S + s];
+      const unsigned long long* w = a.ws + 2 * ((size_t)grp * a.S + s);
+      const float2 p = make_float2(untag(w[0]), untag(w[1]));
       const long long s0 = (long long)s * a.slice_vec;
       const long long s1 = s0 + a.slice_vec < lv ? s0 + a.slice_vec : lv;
       const Moments m = {(float)((s1 - s0) * VW), p.x, p.y};
@@ -350,24 +371,202 @@ __global__ __launch_bounds__(kGnSliceThreads) void gn_apply_kernel(const GnArgs 
   }
 }
 
+// One-launch split form (the groups fill less of the chip than their data
+// would need): S workgroups per group, each holding its slice in registers.
+// A workgroup publishes its slice's moments as two tagged 64-bit words
+// (value and call epoch in one word, written and read as relaxed agent-scope
+// atomics: a reader sees either the old word or the whole new one, so no
+// cache write-back or invalidation is needed) and waits until all S slots of
+// its group carry this call's epoch.  The wait is bounded: a workgroup whose
+// partners have not all published within spin_limit polls (they may not be
+// resident yet) computes every slice's moments itself from x, with the same
+// per-slice arithmetic, so the result is the same either way and no
+// workgroup ever waits without end.
+constexpr int kGnCoopThreads = 256, kGnCoopMaxRv = 8, kGnCoopMaxSlices = 64;
+
+// Moments of slice s (vectors v0 + tid + k * NT), two passes per thread, merged
+// over the workgroup; with `load` the slice is read into raw first.
+template <class E, bool kVec, int RV, int NT>
+__device__ Moments slice_moments(const GnArgs& a, size_t base, long long lv, int s,
+                                 typename GnIo<E, kVec>::Raw (&raw)[RV], bool load, Moments* lds) {
+  using IO = GnIo<E, kVec>;
+  constexpr int VW = IO::VW;
+  const int tid = threadIdx.x;
+  const long long v0 = (long long)s * a.slice_vec;
+  const long long v1 = v0 + a.slice_vec < lv ? v0 + a.slice_vec : lv;
+  if (load) {
+#pragma unroll
+    for (int k = 0; k < RV; ++k) {
+      const long long v = v0 + tid + (long long)k * NT;
+      if (v < v1) raw[k] = IO::load(a.x, base, v);
+    }
+  }
+  float n = 0.f, sum = 0.f;
+#pragma unroll
+  for (int k = 0; k < RV; ++k) {
+    if (v0 + tid + (long long)k * NT < v1) {
+      float f[VW];
+      IO::unpack(raw[k], f);
+#pragma unroll
+      for (int i = 0; i < VW; ++i) sum += f[i];
+      n += (float)VW;
+    }
+  }
+  Moments t = {n, n > 0.f ? sum / n : 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < RV; ++k) {
+    if (v0 + tid + (long long)k * NT < v1) {
+      float f[VW];
+      IO::unpack(raw[k], f);
+#pragma unroll
+      for (int i = 0; i < VW; ++i) t.m2 += (f[i] - t.mean) * (f[i] - t.mean);
+    }
+  }
+  return block_merge<NT>(t, lds);
+}
+
+// (mean, rstd) of a group from its S slice moments, merged on wave 0 in a
+// fixed order: lane j takes slices j, j + 64, ..., then the lanes merge.
+template <int VW>
+__device__ void merge_slices(const GnArgs& a, const float2* parts, long long lv, float2* coef) {
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    Moments g = {0.f, 0.f, 0.f};
+    for (int s = tid; s < a.S; s += 64) {
+      const float2 p = parts[s];
+      const long long s0 = (long long)s * a.slice_vec;
+      const long long s1 = s0 + a.slice_vec < lv ? s0 + a.slice_vec : lv;
+      const Moments m = {(float)((s1 - s0) * VW), p.x, p.y};
+      merge(g, m);
+    }
+    g = wave_merge(g);
+    if (tid == 0) *coef = make_float2(g.mean, 1.f / __builtin_sqrtf(g.m2 / (float)a.L + a.eps));
+  }
+}
+
+template <class E, bool kVec, int RV>
+__global__ __launch_bounds__(kGnCoopThreads) void gn_coop_kernel(const GnArgs a) {
+  using IO = GnIo<E, kVec>;
+  constexpr int VW = IO::VW;
+  __shared__ Moments lds[kGnCoopThreads / 64];
+  __shared__ float2 parts[kGnCoopMaxSlices];
+  __shared__ float2 coef;
+  __shared__ int synced;
+  const int tid = threadIdx.x;
+  const int grp = blockIdx.x / a.S, sl = blockIdx.x - grp * a.S;
+  const size_t base = (size_t)grp * a.L;
+  const long long lv = a.L / VW;
+  typename IO::Raw raw[RV];
+  const Moments mine = slice_moments<E, kVec, RV, kGnCoopThreads>(a, base, lv, sl, raw, true, lds);
+  if (tid == 0) {
+    unsigned long long* w = a.ws + 2 * (size_t)blockIdx.x;
+    __hip_atomic_store(w, tag(mine.mean, a.epoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(w + 1, tag(mine.m2, a.epoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (tid < 64) {
+    // lane j polls slot j of the group (S <= 64)
+    unsigned long long* w = a.ws + 2 * ((size_t)grp * a.S + tid);
+    unsigned long long w0 = 0, w1 = 0;
+    bool ready = tid >= a.S;
+    for (int i = 0; i <= a.spin_limit; ++i) {
+      if (!ready) {
+        w0 = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        w1 = __hip_atomic_load(w + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ready = (unsigned)(w0 >> 32) == a.epoch && (unsigned)(w1 >> 32) == a.epoch;
+      }
+      if (__all(ready) || i == a.spin_limit) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (tid < a.S) parts[tid] = make_float2(untag(w0), untag(w1));
+    const bool all_ready = __all(ready);
+    if (tid == 0) synced = all_ready;
+  }
+  __syncthreads();
+  if (synced) {
+    merge_slices<VW>(a, parts, lv, &coef);
+  } else {
+    // partners not (yet) resident: every slice's moments from x, as they
+    // would have computed them, then this slice again for the output
+    for (int s = 0; s < a.S; ++s) {
+      const Moments m = slice_moments<E, kVec, RV, kGnCoopThreads>(a, base, lv, s, raw, true, lds);
+      if (tid == 0) parts[s] = make_float2(m.mean, m.m2);
+    }
+    __syncthreads();
+    merge_slices<VW>(a, parts, lv, &coef);
+    (void)slice_moments<E, kVec, RV, kGnCoopThreads>(a, base, lv, sl, raw, true, lds);
+  }
+  __syncthreads();
+  const float mean = coef.x, rstd = coef.y;
+  const int gin = grp % a.G;
+  const long long v0 = (long long)sl * a.slice_vec;
+  const long long v1 = v0 + a.slice_vec < lv ? v0 + a.slice_vec : lv;
+#pragma unroll
+  for (int k = 0; k < RV; ++k) {
+    const long long v = v0 + tid + (long long)k * kGnCoopThreads;
+    if (v < v1) {
+      float f[VW];
+      IO::unpack(raw[k], f);
+      gn_write<E, kVec>(a, gin, base, v, f, mean, rstd);
+    }
+  }
+}
+
 // The launch plan of one problem: fused (RV vectors per thread) or two
 // launches over S slices per group.
 struct GnPlan {
   bool vec;
   int rv;            // > 0: fused with rv vectors per thread
-  long long s;       // slices per group (two-launch path)
+  int coop_rv;       // > 0: one-launch split form with coop_rv vectors per thread
+  long long s;       // slices per group (split forms)
   long long slice_vec;
   size_t ws_bytes;   // workspace the plan needs
 };
 
-// ATTN_GN_PATH=split / fused forces a path (for measurements; fused only
-// where the group fits).
+// ATTN_GN_PATH=split / fused / coop forces a form (for measurements; fused
+// and coop only where they fit).
 int forced_path() {
   const char* e = std::getenv("ATTN_GN_PATH");
   if (!e) return 0;
   if (!std::strcmp(e, "split")) return 1;
   if (!std::strcmp(e, "fused")) return 2;
+  if (!std::strcmp(e, "coop")) return 3;
   return 0;
+}
+
+// Epoch of a call: nonzero and new for every call (a zero-filled workspace
+// holds epoch 0 and earlier calls' words hold earlier epochs; the counter
+// repeats only after 2^32 - 1 calls).
+unsigned next_epoch() {
+  static std::atomic<unsigned> counter{0};
+  unsigned e = counter.fetch_add(1u, std::memory_order_relaxed) + 1u;
+  if (e == 0u) e = counter.fetch_add(1u, std::memory_order_relaxed) + 1u;
+  return e;
+}
+
+// Polls before a one-launch split workgroup computes its group's moments on
+// its own (ATTN_GN_SPIN overrides, e.g. 0 to exercise that path).
+int spin_limit() {
+  const char* e = std::getenv("ATTN_GN_SPIN");
+  return e ? std::atoi(e) : (1 << 16);
+}
+
+// Workgroups of `kern` (256 threads) resident at once on the current device.
+int resident_wgs(const void* kern) {
+  int dev = 0, per_cu = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kGnCoopThreads, 0) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return per_cu * cus;
+}
+
+template <class E, bool kVec>
+const void* coop_kernel(int rv) {
+  switch (rv) {
+    case 1: return (const void*)gn_coop_kernel<E, kVec, 1>;
+    case 2: return (const void*)gn_coop_kernel<E, kVec, 2>;
+    case 4: return (const void*)gn_coop_kernel<E, kVec, 4>;
+    default: return (const void*)gn_coop_kernel<E, kVec, 8>;
+  }
 }
 
 template <class E>
@@ -378,6 +577,7 @@ GnPlan gn_plan(const GroupNormProblem& p) {
   const long long L = (long long)(p.C / p.G) * p.HW, lv = L / VW;
   const long long ng = (long long)p.N * p.G;
   pl.rv = 0;
+  pl.coop_rv = 0;
   pl.s = 1;
   pl.slice_vec = lv;
   pl.ws_bytes = 0;
@@ -390,9 +590,35 @@ GnPlan gn_plan(const GroupNormProblem& p) {
   int rv_fit = 0;
   for (int rv = 1; rv <= kGnMaxRv && !rv_fit; rv *= 2)
     if ((long long)rv * kGnFusedThreads >= lv) rv_fit = rv;
-  if (rv_fit && forced != 1 && (forced == 2 || ng >= kGnFusedMinGroups || rv_fit <= 2)) {
+  if (rv_fit && forced != 1 && forced != 3 && (forced == 2 || ng >= kGnFusedMinGroups || rv_fit <= 2)) {
     pl.rv = rv_fit;
     return pl;
+  }
+  // Split forms: the workspace holds 16 bytes of tagged moments per slice.
+  pl.coop_rv = 0;
+  if (forced != 1) {
+    // one launch: about kGnSliceTarget workgroups, slices of at most
+    // kGnCoopMaxRv vectors per thread, at most kGnCoopMaxSlices per group,
+    // all workgroups resident at once
+    const long long cap_slice = (long long)kGnCoopThreads * kGnCoopMaxRv;
+    long long sc = (kGnSliceTarget + ng - 1) / ng;
+    const long long s_min = (lv + cap_slice - 1) / cap_slice;
+    const long long s_max = (lv + kGnCoopThreads - 1) / kGnCoopThreads;  // a vector per thread at least
+    if (sc > s_max) sc = s_max;
+    if (sc < s_min) sc = s_min;
+    if (sc < 1) sc = 1;
+    const long long sv = (lv + sc - 1) / sc;
+    sc = (lv + sv - 1) / sv;
+    int rv = 1;
+    while ((long long)rv * kGnCoopThreads < sv) rv *= 2;
+    if (sc >= 2 && sc <= kGnCoopMaxSlices && rv <= kGnCoopMaxRv &&
+        ng * sc <= resident_wgs(pl.vec ? coop_kernel<E, true>(rv) : coop_kernel<E, false>(rv))) {
+      pl.coop_rv = rv;
+      pl.s = sc;
+      pl.slice_vec = sv;
+      pl.ws_bytes = (size_t)(ng * sc) * 16;
+      return pl;
+    }
   }
   // two launches: about kGnSliceTarget workgroups, each slice at least one
   // full batch of vectors per thread
@@ -403,7 +629,7 @@ GnPlan gn_plan(const GroupNormProblem& p) {
   if (s < 1) s = 1;
   pl.slice_vec = (lv + s - 1) / s;
   pl.s = (lv + pl.slice_vec - 1) / pl.slice_vec;  // every slice non-empty
-  pl.ws_bytes = (size_t)(ng * pl.s) * sizeof(float2);
+  pl.ws_bytes = (size_t)(ng * pl.s) * 16;
   return pl;
 }
 
@@ -419,7 +645,9 @@ hipError_t launch_gn_t(const GroupNormProblem& p, const GnPlan& pl) {
   a.gamma = p.gamma;
   a.beta = p.beta;
   a.y = p.y;
-  a.ws = (float2*)p.workspace;
+  a.ws = (unsigned long long*)p.workspace;
+  a.epoch = next_epoch();
+  a.spin_limit = spin_limit();
   a.HW = p.HW;
   a.G = p.G;
   a.Cg = p.C / p.G;
@@ -442,6 +670,15 @@ hipError_t launch_gn_t(const GroupNormProblem& p, const GnPlan& pl) {
   }
   const long long grid = ng * pl.s;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (pl.coop_rv > 0) {
+    switch (pl.coop_rv) {
+      case 1: hipLaunchKernelGGL((gn_coop_kernel<E, kVec, 1>), dim3((unsigned)grid), dim3(kGnCoopThreads), 0, p.stream, a); break;
+      case 2: hipLaunchKernelGGL((gn_coop_kernel<E, kVec, 2>), dim3((unsigned)grid), dim3(kGnCoopThreads), 0, p.stream, a); break;
+      case 4: hipLaunchKernelGGL((gn_coop_kernel<E, kVec, 4>), dim3((unsigned)grid), dim3(kGnCoopThreads), 0, p.stream, a); break;
+      default: hipLaunchKernelGGL((gn_coop_kernel<E, kVec, 8>), dim3((unsigned)grid), dim3(kGnCoopThreads), 0, p.stream, a); break;
+    }
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((gn_partial_kernel<E, kVec>), dim3((unsigned)grid), dim3(kGnSliceThreads), 0, p.stream, a);
   hipLaunchKernelGGL((gn_apply_kernel<E, kVec>), dim3((unsigned)grid), dim3(kGnSliceThreads), 0, p.stream, a);
   return hipGetLastError();

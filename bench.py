@@ -286,8 +286,8 @@ def unet_op_records(steps: int, dtype: str = "f16"):
         beta = torch.zeros(C, device="cuda", dtype=tdt)
         y = torch.empty_like(x)
         by = 2 * x.numel() * es + 2 * C * es
-        for path in ("auto", "split", "fused"):
-            # 'split' / 'fused' force one form (ATTN_GN_PATH) for comparison
+        for path in ("auto", "split", "fused", "coop"):
+            # 'split' / 'fused' / 'coop' force one form (ATTN_GN_PATH) for comparison
             if path != "auto":
                 os.environ["ATTN_GN_PATH"] = path
             fn = (lambda: attn.group_norm(x, 32, gamma, beta, eps=1e-5, out=y))

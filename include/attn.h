@@ -194,10 +194,12 @@ attn_status attn_scores_pv(const float* a, const float* ml, const void* v, void*
  * fp16/bf16 or 65536 fp32 elements when x, y are 16-byte aligned and HW*size
  * is a multiple of 16 bytes; 16384 elements otherwise) and the groups fill
  * the chip or are small, it is normalised in one launch, x read once, with
- * no intermediate tensor.  Otherwise two launches over slices of the groups
- * run, with a workspace of attn_group_norm_workspace_size() bytes (device
- * memory, 8-byte aligned, no initialisation; calls sharing one workspace must
- * not overlap in time); workspace may be NULL when that size is 0.
+ * no intermediate tensor.  Otherwise the groups are split over several
+ * workgroups -- in one launch when they can all be resident, else in two --
+ * with a workspace of attn_group_norm_workspace_size() bytes (device memory,
+ * 8-byte aligned, zero-filled before its first use; the kernels leave it
+ * ready for the next call of any shape; calls sharing one workspace must not
+ * overlap in time); workspace may be NULL when that size is 0.
  * Requirements: sizes >= 1, C a multiple of G, eps finite and >= 0, pointers
  * aligned to the element size, (C/G)*HW < 2^31, N*C*HW < 2^40; else
  * ATTN_ERR_INVALID_ARG before anything is launched (also for a missing or

@@ -123,6 +123,35 @@ def test_group_norm_two_launch_path_forced(C, HW, monkeypatch):
         _gn_case(2, C, HW, 32, dtype, seed=C + HW + 1)
 
 
+@pytest.mark.parametrize("C,HW", [(320, 4096), (960, 4096), (1280, 1024), (640, 16384), (64, 999)],
+                         ids=lambda v: str(v))
+def test_group_norm_one_launch_split_forced(C, HW, monkeypatch):
+    # groups split over workgroups that exchange moments in one launch
+    monkeypatch.setenv("ATTN_GN_PATH", "coop")
+    for dtype in ("f16", "bf16", "f32"):
+        _gn_case(2, C, HW, 32, dtype, seed=C + HW + 2)
+
+
+def test_group_norm_bounded_wait_fallback_is_identical(monkeypatch):
+    """With no polls allowed, every workgroup that is not last to arrive
+    computes all of its group's slice moments itself: the output must be the
+    same bits as when the workgroups exchange them."""
+    import torch
+    import attention_attn_stats_amd as attn
+    for shape, dt in (((2, 320, 64 * 64), torch.float16), ((2, 960, 64 * 64), torch.bfloat16),
+                      ((2, 64, 999), torch.float32)):
+        x = torch.randn(shape, device="cuda", generator=torch.Generator(device="cuda").manual_seed(3)).to(dt)
+        monkeypatch.setenv("ATTN_GN_PATH", "coop")
+        y0 = attn.group_norm(x, 32)
+        monkeypatch.setenv("ATTN_GN_SPIN", "0")
+        y1 = attn.group_norm(x, 32)
+        monkeypatch.delenv("ATTN_GN_SPIN")
+        y2 = attn.group_norm(x, 32)  # and the counters were left ready
+        torch.cuda.synchronize()
+        assert torch.equal(y0, y1), f"{shape}: the fallback differs"
+        assert torch.equal(y0, y2), f"{shape}: a second exchange differs"
+
+
 @pytest.mark.parametrize("rv_elems", [1000, 9000, 20000, 40000, 70000, 130000])
 def test_group_norm_every_register_depth(rv_elems, monkeypatch):
     # groups of about rv_elems fp16 elements in one launch: 1, 2, 4, 8, 16
