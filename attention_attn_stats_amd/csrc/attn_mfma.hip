@@ -154,10 +154,12 @@ __device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
 // partially fused softmax.
 //
 // One workgroup = QG query groups of 32 queries x 2 key halves (QG = 8, a
-// 1024-thread workgroup per CU, at d = 40; QG = 4 otherwise); the two waves of
-// a query group walk alternate key blocks (the key range is split in two, as
-// in the block-split reduction; 64-key blocks at d = 40, 32 otherwise) and
-// merge their partial (m, l, O) through LDS at the end.  K and V blocks go
+// 1024-thread workgroup per CU, at d = 40; 4 at d = 80; 2 at d = 160; halved
+// when the problem has fewer workgroups than CUs); the two waves of a query
+// group walk alternate key blocks (the key range is split in two, as in the
+// block-split reduction; 64-key blocks at d = 40 and for the single pass at
+// d = 80, 32 otherwise) and merge their partial (m, l, O) through LDS at the
+// end.  K and V blocks go
 // through a ring of LDS slots per key half, filled cooperatively by that
 // half's waves; more query groups per workgroup means fewer K/V copies per
 // query from L2 into LDS.

@@ -42,8 +42,15 @@ def log(*a):
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel source without its comments and blank space, so
+    that a comment edit does not orphan counters taken on the same code."""
+    import re
+    with open(KERNEL_SRC) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    src = "\n".join(ln.strip() for ln in src.splitlines() if ln.strip())
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
 def load_traffic(kernel: str, workload: str):
