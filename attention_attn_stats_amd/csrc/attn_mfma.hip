@@ -600,6 +600,9 @@ __global__ __launch_bounds__((Shape<D, MODE, kHalfQ>::T)) void fwd_kernel(const 
     const float mtB = ex[(XO + qt * 4 + 1) * 64];
     const float lB = ex[(XO + qt * 4 + 2) * 64];
     const float lrB = ex[(XO + qt * 4 + 3) * 64];
+    // the sums below are written as explicit FMAs: left to the compiler,
+    // the contraction may differ between the workgroup shapes and with it
+    // the last bit of O
     float fA = 1.f, fB = 1.f, M = mo[qt];
     if constexpr (!kPVLike) {
       // a half that saw no key holds (-inf, 0, 0) and contributes nothing
@@ -610,9 +613,10 @@ __global__ __launch_bounds__((Shape<D, MODE, kHalfQ>::T)) void fwd_kernel(const 
 #pragma unroll
     for (int mt = 0; mt < (kStats ? 0 : MT); ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[qt][mt][i] = o[qt][mt][i] * fA + ex[((qt * MT + mt) * 4 + i) * 64] * fB;
-    const float l = lo[qt] * fA + lB * fB;
-    const float lr = lro[qt] * fA + lrB * fB;
+      for (int i = 0; i < 4; ++i)
+        o[qt][mt][i] = __builtin_fmaf(o[qt][mt][i], fA, ex[((qt * MT + mt) * 4 + i) * 64] * fB);
+    const float l = __builtin_fmaf(lo[qt], fA, lB * fB);
+    const float lr = __builtin_fmaf(lro[qt], fA, lrB * fB);
     const float mt_all = __builtin_fmaxf(mto[qt], mtB);
     const int row = qbase + qt * 16 + li;
     float inv = 0.f;
@@ -621,7 +625,7 @@ __global__ __launch_bounds__((Shape<D, MODE, kHalfQ>::T)) void fwd_kernel(const 
         // P was formed against mref = the given m (M here); the given l is
         // relative to it
         const float2 st = *(const float2*)(ml + ((size_t)head * Nq + row) * 2);
-        inv = __builtin_amdgcn_exp2f(M - st.x * kLog2e) / st.y;
+        inv = __builtin_amdgcn_exp2f(__builtin_fmaf(-st.x, kLog2e, M)) / st.y;
       } else {
         inv = 1.f / l;
       }

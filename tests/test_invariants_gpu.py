@@ -177,16 +177,18 @@ def test_bitwise_repeatable_and_stream_independent(name):
 
 
 @pytest.mark.parametrize("d,qwg", [(40, 256), (80, 128), (160, 64)])
-@pytest.mark.parametrize("form", FORMS)
-def test_workgroup_shape_does_not_change_results(d, qwg, form):
+@pytest.mark.parametrize("form", FORMS + ("flash_o",))
+@pytest.mark.parametrize("Nk", [300, 1000])
+def test_workgroup_shape_does_not_change_results(d, qwg, form, Nk):
     """A problem with fewer workgroups than CUs runs with half the query groups
     per workgroup; each wave does the same work either way.  Row i depends on
     q_i, K and V only, so the first rows of a problem one workgroup short of
     filling the chip (halved shape) equal those of one that fills it (default
-    shape) bit for bit."""
+    shape) bit for bit.  flash_o is the single pass without (m, l) out, whose
+    fp16 form tests the rescale on the packed P."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    dtype, Nk = "f16", 300
+    dtype = "f16"
     n_big = cus * qwg
     n_small = (cus - 1) * qwg
     q = synth.tensor(71 + d, (1, 1, n_big, d), dtype)
@@ -194,10 +196,18 @@ def test_workgroup_shape_does_not_change_results(d, qwg, form):
     v = synth.tensor(73 + d, (1, 1, Nk, d), dtype)
     scale = float(np.float32(1 / np.sqrt(d)))
     tk, tv = to_device(k, dtype), to_device(v, dtype)
-    o_big, ml_big = _forward(to_device(q, dtype), tk, tv, form, scale)
-    o_small, ml_small = _forward(to_device(np.ascontiguousarray(q[:, :, :n_small]), dtype), tk, tv, form, scale)
+
+    def run(qh):
+        if form == "flash_o":
+            import attention_attn_stats_amd as attn
+            return attn.flash(qh, tk, tv, scale=scale), None
+        return _forward(qh, tk, tv, form, scale)
+
+    o_big, ml_big = run(to_device(q, dtype))
+    o_small, ml_small = run(to_device(np.ascontiguousarray(q[:, :, :n_small]), dtype))
     torch.cuda.synchronize()
     assert torch.equal(o_small, o_big[:, :, :n_small]), f"d={d} {form}: O differs between workgroup shapes"
-    assert torch.equal(ml_small, ml_big[:, :, :n_small])
+    if ml_big is not None:
+        assert torch.equal(ml_small, ml_big[:, :, :n_small])
     o_ref, ml_ref = reference(q[:, :, :512], k, v, dtype, scale)
     assert_close_o(from_device(o_small)[:, :, :512], o_ref, dtype, f"d={d} {form} halved shape")
