@@ -198,6 +198,15 @@ def time_steps(cfg, form: str, steps: int, warmup: int, cold: bool):
     if form == "pf_scores":
         r["second_kernel_median_ms"] = statistics.median([e[1].elapsed_time(e[3]) for e in ev])
         r["third_kernel_median_ms"] = statistics.median([e[3].elapsed_time(e[2]) for e in ev])
+    if not cold and form in ("flash", "pf"):
+        # GPU time alone: the form's launches replayed back to back from a graph
+        if form == "flash":
+            fn = lambda: attn.flash(q, k, v, out=out, scale=cfg.scale)
+        else:
+            def fn():
+                attn.stats(q, k, ml=ml, scale=cfg.scale)
+                attn.pv(q, k, v, ml, out=out, scale=cfg.scale)
+        r["graph_ms"] = _time_graph(fn)
     return r
 
 
@@ -214,6 +223,11 @@ def config_record(cfg, form: str, steps: int, cold: bool) -> dict:
            "pct_peak": round(100 * cfg.flops / (t["median_ms"] * 1e-3) / 1e12 / peak, 2),
            "algorithmic_bytes": by[form], "t_roof_us": round(t_roof * 1e6, 3),
            "roofline_frac": round(t_roof / (t["median_ms"] * 1e-3), 4)}
+    if "graph_ms" in t:
+        tg = t["graph_ms"] * 1e-3
+        rec["graph_us"] = round(tg * 1e6, 2)
+        rec["graph_tflops"] = round(cfg.flops / tg / 1e12, 2)
+        rec["graph_roofline_frac"] = round(t_roof / tg, 4)
     if form in ("pf", "pf_bnhd"):
         ts = t["first_kernel_median_ms"] * 1e-3
         rec["stats_pass_us"] = round(ts * 1e6, 2)
