@@ -153,16 +153,16 @@ __device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
 // Forward kernel: FlashAttention (online softmax), or either pass of the
 // partially fused softmax.
 //
-// One workgroup = QG query groups of 32 queries x 2 key halves (QG = 8, a
+// One workgroup = QG query groups of 32 queries x KH key splits (QG = 8, a
 // 1024-thread workgroup per CU, at d = 40; 4 at d = 80; 2 at d = 160; halved
-// when the problem has fewer workgroups than CUs); the two waves of a query
-// group walk alternate key blocks (the key range is split in two, as in the
-// block-split reduction; 64-key blocks at d = 40 and for the single pass at
-// d = 80, 32 otherwise) and merge their partial (m, l, O) through LDS at the
-// end.  K and V blocks go
-// through a ring of LDS slots per key half, filled cooperatively by that
-// half's waves; more query groups per workgroup means fewer K/V copies per
-// query from L2 into LDS.
+// when the problem has fewer workgroups than CUs; KH = 2, or 4 for those
+// small d = 80 problems); the KH waves of a query group walk interleaved key
+// blocks (the key range is cut into blocks as in the block-split reduction;
+// 64-key blocks at d = 40 and for the single pass at d = 80 with two splits,
+// 32 otherwise) and merge their partial (m, l, O) through LDS at the end.
+// K and V blocks go through a ring of LDS slots per key split, filled
+// cooperatively by that split's waves; more query groups per workgroup means
+// fewer K/V copies per query from L2 into LDS.
 //
 //   * S^T = K Q^T on 32x32x16 MFMAs: a 32-key x 32-query tile per block, the
 //     head dim in K=16 steps.  Lane l owns query l % 32 and 16 of the 32 keys;
@@ -200,18 +200,22 @@ struct Shape {
   // 7-13 % faster there; the two-pass form stays at 32, where 64 was slower at
   // N >= 4096); 32 otherwise
   static constexpr bool kFlashLike = MODE == kModeFlash || MODE == kModeFlashML;
-  static constexpr int BN = (D == 40 || (D == 80 && kFlashLike)) ? 64 : 32;
+  // key splits per query group: 2, or 4 for the small d = 80 problems that
+  // take the halved shape (twice the waves; 32-key blocks keep the four
+  // rings within LDS)
+  static constexpr int KH = (kHalfQ && D == 80) ? 4 : 2;
+  static constexpr int BN = (D == 40 || (D == 80 && kFlashLike && KH == 2)) ? 64 : 32;
   // query groups per workgroup: d = 160 takes 2 (half the workgroup, twice
   // the workgroups for the small sequences of the UNet's deep levels);
   // kHalfQ halves it again for problems with fewer workgroups than CUs
   static constexpr int QG0 = D == 40 ? 8 : (D == 160 ? 2 : 4);
   static constexpr int QG = kHalfQ && QG0 > 1 ? QG0 / 2 : QG0;
-  static constexpr int W = 2 * QG;               // waves per workgroup (x 2 key halves)
+  static constexpr int W = KH * QG;              // waves per workgroup
   static constexpr int T = 64 * W;               // threads per workgroup
-  static constexpr int HT = 64 * QG;             // threads per key half
+  static constexpr int HT = 64 * QG;             // threads per key split
   static constexpr int QWG = QG * kQ;            // queries per workgroup
   static constexpr int NT = BN / 32;             // 32-key score tiles per block
-  static constexpr int NBUF = D >= 160 ? 2 : 3;  // ring slots per key half
+  static constexpr int NBUF = D >= 160 ? 2 : 3;  // ring slots per key split
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
   static constexpr int SLOT = BN * (PK + PV);    // 16-bit elements per slot (K then V)
   static_assert(D % 8 == 0 && D >= 16, "head dim must be a multiple of 8");
@@ -227,7 +231,7 @@ __global__ __launch_bounds__((Shape<D, MODE, kHalfQ>::T)) void fwd_kernel(const 
                                                  float scale) {
   using S = Shape<D, MODE, kHalfQ>;
   constexpr int KS = S::KS, MT = S::MT, PK = S::PK, PV = S::PV, NBUF = S::NBUF;
-  constexpr int BN = S::BN, NT = S::NT, kQG = S::QG, kHT = S::HT, kQWG = S::QWG;
+  constexpr int BN = S::BN, NT = S::NT, kQG = S::QG, kHT = S::HT, kQWG = S::QWG, KH = S::KH;
   constexpr bool kStats = MODE == kModeStats;
   constexpr bool kFromA = MODE == kModePVScores;             // logits read from A (float32)
   constexpr bool kPVLike = MODE == kModePV || kFromA;        // (m, l) given, O only
@@ -237,19 +241,21 @@ __global__ __launch_bounds__((Shape<D, MODE, kHalfQ>::T)) void fwd_kernel(const 
   constexpr bool kValuSum = !kPVLike && (kStats ? !TR::kRoundedSumOk
                                                        : (!S::kOnes || (kReportML && !TR::kRoundedSumOk)));
   constexpr int MO = kStats ? 1 : MT;  // 16-row tiles of the accumulator (stats: the row sums)
-  // floats per lane handed from one key half to the other in the merge: O
+  // floats per lane handed from one key split to the first in the merge: O
   // (not in the stats form), then 4 per query tile
   constexpr int XO = kStats ? 0 : 2 * MT * 4, NEX = XO + 8;
   // LDS slot: the K block, then the V block (none in the stats form)
   constexpr int SLOT = kStats ? BN * PK : S::SLOT;
-  constexpr int RING = 2 * NBUF * SLOT, XCH = NEX * 64 * kQG * 2;
+  // LDS: a ring per key split; after the walk, an exchange area per split
+  // but the first (floats, counted here in 16-bit elements)
+  constexpr int RING = KH * NBUF * SLOT, XCH = NEX * 64 * kQG * (KH - 1) * 2;
   constexpr int SMEM = RING > XCH ? RING : XCH;
   // fp16 flash without (m, l) out: the rescale test runs on the packed P
   constexpr bool kLazyMax = TR::kPackedMax && MODE == kModeFlash;
   __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int qg = wave % kQG, half = wave / kQG, htid = tid % kHT;
+  const int qg = wave % kQG, split = wave / kQG, htid = tid % kHT;
   const int l32 = lane & 31, hi = lane >> 5;  // 32x32 layout: query l32, key subgroup hi
   const int G = lane >> 4, li = lane & 15;    // 16x16 layout
   // exp2 units: the stored A already carries the scale
@@ -262,10 +268,10 @@ __global__ __launch_bounds__((Shape<D, MODE, kHalfQ>::T)) void fwd_kernel(const 
   const uint16_t* kh = k + head_offset(lay.k, lay.H, head);
   const uint16_t* vh = kStats ? nullptr : v + head_offset(lay.v, lay.H, head);  // the stats form reads no V
   const int qrs = lay.q.row, krs_ = lay.k.row, vrs_ = lay.v.row;  // row strides (elements)
-  uint16_t* const ring = smem + half * NBUF * SLOT;
+  uint16_t* const ring = smem + split * NBUF * SLOT;
 
   if constexpr (S::kOnes) {
-    // padding columns of every slot of this half: zero, except V column D =
+    // padding columns of every slot of this split: zero, except V column D =
     // 1.0 (the row-sum dim)
     for (int e = htid; e < NBUF * BN * (PK - D); e += kHT) {
       const int r = e / (PK - D), col = e - r * (PK - D);
@@ -313,10 +319,10 @@ __global__ __launch_bounds__((Shape<D, MODE, kHalfQ>::T)) void fwd_kernel(const 
   float mtrue = -INFINITY, lsum = 0.f;
 
   const int nblk = (Nk + BN - 1) / BN;
-  const int niter = (nblk + 1) / 2;
-  // Staging of this half's block for iteration `it` (key block 2 it + half).
-  // One job = one 16-byte chunk per lane, one buffer load and one
-  // ds_write_b128 per wave; the half's waves take jobs qg, qg + 4, ...  K
+  const int niter = (nblk + KH - 1) / KH;
+  // Staging of this split's block for iteration `it` (key block KH it +
+  // split).  One job = one 16-byte chunk per lane, one buffer load and one
+  // ds_write_b128 per wave; the split's waves take jobs qg, qg + QG, ...  K
   // chunks go column by column (lane -> key row), V chunks in LDS order over
   // the permuted key rows; both orders write LDS without bank conflicts.  The
   // buffer resource starts at the block's first key and ends at key Nk, so
@@ -331,7 +337,7 @@ __global__ __launch_bounds__((Shape<D, MODE, kHalfQ>::T)) void fwd_kernel(const 
   const __amdgpu_buffer_rsrc_t ars =
       make_rsrc(kFromA ? (const void*)(a + (size_t)head * Nq * Nk) : (const void*)kh, kFromA ? Nq * Nk * 4 : 0);
   const int arow = (qbase + l32) * Nk;
-  const int halfu = __builtin_amdgcn_readfirstlane(half);
+  const int splitu = __builtin_amdgcn_readfirstlane(split);
   const int qgu = __builtin_amdgcn_readfirstlane(qg);
   int goff[JPW], soff[JPW];  // byte offset in the block (< 0: no chunk), element offset in the slot
 #pragma unroll
@@ -353,7 +359,7 @@ __global__ __launch_bounds__((Shape<D, MODE, kHalfQ>::T)) void fwd_kernel(const 
   }
   uint4 stg[JPW];
   auto gload = [&](int it) {
-    const int key0 = (2 * it + halfu) * BN;
+    const int key0 = (KH * it + splitu) * BN;
     // the resources end after the last key's d elements
     // up to 2^32 - 2 bytes (a head holds fewer than 2^31 elements): unsigned
     const unsigned kbytes = Nk > key0 ? ((unsigned)(Nk - key0 - 1) * (unsigned)krs_ + D) * 2u : 0u;
@@ -445,7 +451,7 @@ __global__ __launch_bounds__((Shape<D, MODE, kHalfQ>::T)) void fwd_kernel(const 
   };
 
   for (int it = 0; it < niter; ++it) {
-    const int kb = 2 * it + halfu;  // wave-uniform
+    const int kb = KH * it + splitu;  // wave-uniform
     if (kb < nblk) {
       const uint16_t* Ks = ring + (it % NBUF) * SLOT;
       const uint16_t* Vs = Ks + BN * PK;
@@ -554,7 +560,7 @@ __global__ __launch_bounds__((Shape<D, MODE, kHalfQ>::T)) void fwd_kernel(const 
   }
 
   // ---- per-query state in the 16x16 layout: lane (G, li) <- query qt*16 + li
-  if (nblk <= half) mref = -INFINITY;  // this half saw no key: it must not weigh in the merge
+  if (nblk <= split) mref = -INFINITY;  // this split saw no key: it must not weigh in the merge
   float mo[2], mto[2], lo[2], lro[2];
   const float lfull = kValuSum ? pair_sum32(lsum) : 0.f;
 #pragma unroll
@@ -577,9 +583,12 @@ __global__ __launch_bounds__((Shape<D, MODE, kHalfQ>::T)) void fwd_kernel(const 
     }
   }
 
-  // ---- merge the two key halves: half 1 hands its state to half 0 through LDS
-  float* ex = (float*)smem + qg * NEX * 64 + lane;
-  if (half == 1) {
+  // ---- merge the key splits: splits 1 .. KH-1 hand their state to split 0
+  // through LDS, which folds them in, in that order
+  float* const ex0 = (float*)smem + lane;
+  auto exch = [&](int sp) { return ex0 + ((sp - 1) * kQG + qg) * NEX * 64; };
+  if (split > 0) {
+    float* ex = exch(split);
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
 #pragma unroll
@@ -593,31 +602,40 @@ __global__ __launch_bounds__((Shape<D, MODE, kHalfQ>::T)) void fwd_kernel(const 
     }
   }
   __syncthreads();
-  if (half == 1) return;
+  if (split > 0) return;
+#pragma unroll
+  for (int sp = 1; sp < KH; ++sp) {
+    const float* ex = exch(sp);
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const float mB = ex[(XO + qt * 4 + 0) * 64];
+      const float mtB = ex[(XO + qt * 4 + 1) * 64];
+      const float lB = ex[(XO + qt * 4 + 2) * 64];
+      const float lrB = ex[(XO + qt * 4 + 3) * 64];
+      // the sums below are written as explicit FMAs: left to the compiler,
+      // the contraction may differ between the workgroup shapes and with it
+      // the last bit of O
+      float fA = 1.f, fB = 1.f, M = mo[qt];
+      if constexpr (!kPVLike) {
+        // a split that saw no key holds (-inf, 0, 0) and contributes nothing
+        M = __builtin_fmaxf(mo[qt], mB);
+        fA = __builtin_amdgcn_exp2f(mo[qt] - M);
+        fB = __builtin_amdgcn_exp2f(mB - M);
+      }
+#pragma unroll
+      for (int mt = 0; mt < (kStats ? 0 : MT); ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o[qt][mt][i] = __builtin_fmaf(o[qt][mt][i], fA, ex[((qt * MT + mt) * 4 + i) * 64] * fB);
+      lo[qt] = __builtin_fmaf(lo[qt], fA, lB * fB);
+      lro[qt] = __builtin_fmaf(lro[qt], fA, lrB * fB);
+      mto[qt] = __builtin_fmaxf(mto[qt], mtB);
+      mo[qt] = M;
+    }
+  }
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
-    const float mB = ex[(XO + qt * 4 + 0) * 64];
-    const float mtB = ex[(XO + qt * 4 + 1) * 64];
-    const float lB = ex[(XO + qt * 4 + 2) * 64];
-    const float lrB = ex[(XO + qt * 4 + 3) * 64];
-    // the sums below are written as explicit FMAs: left to the compiler,
-    // the contraction may differ between the workgroup shapes and with it
-    // the last bit of O
-    float fA = 1.f, fB = 1.f, M = mo[qt];
-    if constexpr (!kPVLike) {
-      // a half that saw no key holds (-inf, 0, 0) and contributes nothing
-      M = __builtin_fmaxf(mo[qt], mB);
-      fA = __builtin_amdgcn_exp2f(mo[qt] - M);
-      fB = __builtin_amdgcn_exp2f(mB - M);
-    }
-#pragma unroll
-    for (int mt = 0; mt < (kStats ? 0 : MT); ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        o[qt][mt][i] = __builtin_fmaf(o[qt][mt][i], fA, ex[((qt * MT + mt) * 4 + i) * 64] * fB);
-    const float l = __builtin_fmaf(lo[qt], fA, lB * fB);
-    const float lr = __builtin_fmaf(lro[qt], fA, lrB * fB);
-    const float mt_all = __builtin_fmaxf(mto[qt], mtB);
+    const float M = mo[qt], l = lo[qt], lr = lro[qt], mt_all = mto[qt];
     const int row = qbase + qt * 16 + li;
     float inv = 0.f;
     if (row < Nq) {
@@ -676,7 +694,9 @@ hipError_t launch_fwd_q(const Problem& p, int qtiles, long long nwg) {
 
 // Workgroups of the default shape when they fill the chip; otherwise half
 // the query groups per workgroup and twice the workgroups (every wave does
-// the same work either way, so the results are identical).
+// the same work either way, so the results are identical), and at d = 80
+// also four key splits of 32-key blocks instead of two (twice the waves; the
+// key blocking differs, so the results agree to rounding, not bit for bit).
 template <class TR, int D, int MODE>
 hipError_t launch_fwd_t(const Problem& p) {
   using S = Shape<D, MODE, false>;

@@ -184,8 +184,10 @@ def test_workgroup_shape_does_not_change_results(d, qwg, form, Nk):
     per workgroup; each wave does the same work either way.  Row i depends on
     q_i, K and V only, so the first rows of a problem one workgroup short of
     filling the chip (halved shape) equal those of one that fills it (default
-    shape) bit for bit.  flash_o is the single pass without (m, l) out, whose
-    fp16 form tests the rescale on the packed P."""
+    shape) bit for bit.  At d = 80 the halved shape also cuts the keys into
+    four splits of 32-key blocks instead of two: there the two agree to the
+    rounding bound instead.  flash_o is the single pass without (m, l) out,
+    whose fp16 form tests the rescale on the packed P."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     dtype = "f16"
@@ -206,8 +208,17 @@ def test_workgroup_shape_does_not_change_results(d, qwg, form, Nk):
     o_big, ml_big = run(to_device(q, dtype))
     o_small, ml_small = run(to_device(np.ascontiguousarray(q[:, :, :n_small]), dtype))
     torch.cuda.synchronize()
-    assert torch.equal(o_small, o_big[:, :, :n_small]), f"d={d} {form}: O differs between workgroup shapes"
-    if ml_big is not None:
-        assert torch.equal(ml_small, ml_big[:, :, :n_small])
-    o_ref, ml_ref = reference(q[:, :, :512], k, v, dtype, scale)
-    assert_close_o(from_device(o_small)[:, :, :512], o_ref, dtype, f"d={d} {form} halved shape")
+    if d != 80:
+        assert torch.equal(o_small, o_big[:, :, :n_small]), f"d={d} {form}: O differs between workgroup shapes"
+        if ml_big is not None:
+            assert torch.equal(ml_small, ml_big[:, :, :n_small])
+    else:
+        diff = (o_small.float() - o_big[:, :, :n_small].float()).abs().max().item()
+        assert diff <= 2.0 ** -8, f"d={d} {form}: shapes differ by {diff}"
+        if ml_big is not None:
+            assert_close_ml(from_device(ml_small), from_device(ml_big[:, :, :n_small]), f"d={d} {form} shapes")
+    for rows in (slice(0, 512), slice(n_small - 300, n_small)):
+        o_ref, ml_ref = reference(q[:, :, rows], k, v, dtype, scale)
+        assert_close_o(from_device(o_small)[:, :, rows], o_ref, dtype, f"d={d} {form} halved shape")
+        if ml_small is not None:
+            assert_close_ml(from_device(ml_small)[:, :, rows], ml_ref, f"d={d} {form} halved shape")
