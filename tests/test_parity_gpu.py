@@ -81,6 +81,7 @@ RAGGED = [
     (1, 1, 129, 63, 40),
     (2, 1, 300, 129, 80),
     (1, 3, 33, 31, 80),
+    (1, 2, 100, 65, 80),   # four key splits of 32 keys: three blocks, the last of one key
     (1, 2, 17, 33, 160),
     (2, 1, 140, 97, 160),
     (1, 1, 64, 1, 160),
