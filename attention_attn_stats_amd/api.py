@@ -31,19 +31,23 @@ def _check(status: int, where: str):
 
 
 def _dims(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None):
-    if q.dim() != 4 or k.dim() != 4:
+    # (every attribute read costs a fraction of a microsecond: each is read once)
+    qs, ks = q.shape, k.shape
+    if len(qs) != 4 or len(ks) != 4:
         raise ValueError("q and k must be [B, H, N, d]")
-    B, H, Nq, d = q.shape
-    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != d:
-        raise ValueError(f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
-    if v is not None and v.shape != k.shape:
-        raise ValueError(f"v shape {tuple(v.shape)} must equal k shape {tuple(k.shape)}")
-    for t in (q, k) + ((v,) if v is not None else ()):
-        if not t.is_cuda or t.dtype != q.dtype or (t.stride(3) != 1 and t.shape[3] > 1):
+    B, H, Nq, d = qs
+    Bk, Hk, Nk, dk = ks
+    if Bk != B or Hk != H or dk != d:
+        raise ValueError(f"k shape {tuple(ks)} does not match q {tuple(qs)}")
+    if v is not None and v.shape != ks:
+        raise ValueError(f"v shape {tuple(v.shape)} must equal k shape {tuple(ks)}")
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported dtype {dt}")
+    for t in (q, k, v):
+        if t is not None and (not t.is_cuda or t.dtype != dt or (d > 1 and t.stride(3) != 1)):
             raise ValueError("q, k, v must be device tensors of one dtype with contiguous rows")
-    if q.dtype not in _DT:
-        raise ValueError(f"unsupported dtype {q.dtype}")
-    return B, H, Nq, k.shape[2], d
+    return B, H, Nq, Nk, d
 
 
 def _strides(t: torch.Tensor) -> _lib.Strides:
@@ -57,8 +61,8 @@ def _strides(t: torch.Tensor) -> _lib.Strides:
 def _layout(q, k, v=None, out=None):
     """None when every tensor is dense (the plain entry points), else the
     attn_layout of their strides."""
-    ts = [t for t in (q, k, v, out) if t is not None]
-    if all(t.is_contiguous() for t in ts):
+    if (q.is_contiguous() and k.is_contiguous() and (v is None or v.is_contiguous())
+            and (out is None or out.is_contiguous())):
         return None
     z = _lib.Strides(0, 0, 0)
     return _lib.Layout(_strides(q), _strides(k), _strides(v) if v is not None else z,
@@ -70,7 +74,8 @@ def _out_for(q, out):
         return torch.empty_like(q)  # keeps q's strides when q is a dense view
     if out.shape != q.shape or out.dtype != q.dtype or not out.is_cuda or out.stride(3) != 1:
         raise ValueError("out must be a device tensor of q's shape and dtype with contiguous rows")
-    if torch._debug_has_internal_overlap(out) == 1:
+    # (a contiguous tensor cannot overlap itself)
+    if not out.is_contiguous() and torch._debug_has_internal_overlap(out) == 1:
         raise ValueError("out must not have overlapping elements")
     return out
 
@@ -79,8 +84,17 @@ def _scale(scale, d):
     return float(1.0 / math.sqrt(d)) if scale is None else float(scale)
 
 
-def _stream():
-    return ctypes_stream(torch.cuda.current_stream())
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(t: torch.Tensor | None = None):
+    """The current stream of t's device (else of the current device) as the
+    handle the library takes; read without building a torch Stream object
+    where torch offers that."""
+    dev = t.get_device() if t is not None else torch.cuda.current_device()
+    if _raw_stream is not None:
+        return _raw_stream(dev)
+    return ctypes_stream(torch.cuda.current_stream(dev))
 
 
 def ctypes_stream(s: torch.cuda.Stream):
@@ -101,7 +115,7 @@ def stats(q, k, ml=None, scale=None):
     B, H, Nq, Nk, d = _dims(q, k, None)
     ml = _ml_for(q, ml)
     lay = _layout(q, k)
-    args = (B, H, Nq, Nk, d, _scale(scale, d), _DT[q.dtype], _stream())
+    args = (B, H, Nq, Nk, d, _scale(scale, d), _DT[q.dtype], _stream(q))
     if lay is None:
         _check(_lib.load().attn_stats(q.data_ptr(), k.data_ptr(), ml.data_ptr(), *args), "attn_stats")
     else:
@@ -118,7 +132,7 @@ def pv(q, k, v, ml, out=None, scale=None):
     out = _out_for(q, out)
     lay = _layout(q, k, v, out)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), ml.data_ptr(), out.data_ptr())
-    args = (B, H, Nq, Nk, d, _scale(scale, d), _DT[q.dtype], _stream())
+    args = (B, H, Nq, Nk, d, _scale(scale, d), _DT[q.dtype], _stream(q))
     if lay is None:
         _check(_lib.load().attn_pv(*ptrs, *args), "attn_pv")
     else:
@@ -135,7 +149,7 @@ def flash(q, k, v, out=None, ml=None, want_ml=False, scale=None):
         ml = _ml_for(q, ml)
     lay = _layout(q, k, v, out)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), ml.data_ptr() if ml is not None else None)
-    args = (B, H, Nq, Nk, d, _scale(scale, d), _DT[q.dtype], _stream())
+    args = (B, H, Nq, Nk, d, _scale(scale, d), _DT[q.dtype], _stream(q))
     if lay is None:
         _check(_lib.load().attn_flash(*ptrs, *args), "attn_flash")
     else:
@@ -152,7 +166,7 @@ def forward(q, k, v, variant="auto", out=None, ml=None, scale=None):
     ml = _ml_for(q, ml)
     lay = _layout(q, k, v, out)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), ml.data_ptr())
-    args = (B, H, Nq, Nk, d, _scale(scale, d), _VAR[variant], _DT[q.dtype], _stream())
+    args = (B, H, Nq, Nk, d, _scale(scale, d), _VAR[variant], _DT[q.dtype], _stream(q))
     if lay is None:
         _check(_lib.load().attn_forward(*ptrs, *args), "attn_forward")
     else:
@@ -175,7 +189,7 @@ def scores(q, k, a=None, scale=None):
         raise ValueError("scores() takes contiguous q and k")
     a = _a_for(B, H, Nq, Nk, q.device, a)
     _check(_lib.load().attn_scores(q.data_ptr(), k.data_ptr(), a.data_ptr(), B, H, Nq, Nk, d,
-                                   _scale(scale, d), _DT[q.dtype], _stream()), "attn_scores")
+                                   _scale(scale, d), _DT[q.dtype], _stream(q)), "attn_scores")
     return a
 
 
@@ -188,7 +202,7 @@ def scores_stats(a, ml=None):
         ml = torch.empty((B, H, Nq, 2), device=a.device, dtype=torch.float32)
     elif ml.shape != (B, H, Nq, 2) or ml.dtype != torch.float32 or not ml.is_contiguous() or not ml.is_cuda:
         raise ValueError("ml must be a contiguous float32 [B, H, Nq, 2] device tensor")
-    _check(_lib.load().attn_scores_stats(a.data_ptr(), ml.data_ptr(), B, H, Nq, Nk, _stream()),
+    _check(_lib.load().attn_scores_stats(a.data_ptr(), ml.data_ptr(), B, H, Nq, Nk, _stream(a)),
            "attn_scores_stats")
     return ml
 
@@ -209,7 +223,7 @@ def scores_pv(a, ml, v, out=None):
     if out.shape != (B, H, Nq, d) or out.dtype != v.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous [B, H, Nq, d] tensor of v's dtype")
     _check(_lib.load().attn_scores_pv(a.data_ptr(), ml.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, Nq, Nk,
-                                      d, _DT[v.dtype], _stream()), "attn_scores_pv")
+                                      d, _DT[v.dtype], _stream(a)), "attn_scores_pv")
     return out
 
 
@@ -219,7 +233,8 @@ _GN_WS = {}
 def _gn_workspace(device, nbytes: int) -> torch.Tensor:
     """A group-normalisation workspace of at least nbytes, one per device and
     stream (kernels on one stream never overlap, so they may share it)."""
-    key = (device, torch.cuda.current_stream(device).cuda_stream)
+    key = (device, _raw_stream(device.index) if _raw_stream is not None
+           else torch.cuda.current_stream(device).cuda_stream)
     ws = _GN_WS.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)  # zero-filled before first use
@@ -247,7 +262,7 @@ def group_norm(x, groups: int, gamma=None, beta=None, eps: float = 1e-5, out=Non
     _check(lib.attn_group_norm(x.data_ptr(), gamma.data_ptr() if gamma is not None else None,
                                beta.data_ptr() if beta is not None else None, out.data_ptr(),
                                ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
-                               N, C, HW, int(groups), float(eps), _DT[x.dtype], _stream()), "attn_group_norm")
+                               N, C, HW, int(groups), float(eps), _DT[x.dtype], _stream(x)), "attn_group_norm")
     return out
 
 
@@ -261,7 +276,7 @@ def geglu(h, out=None):
     out = torch.empty(shape, device=h.device, dtype=h.dtype) if out is None else out
     if tuple(out.shape) != shape or out.dtype != h.dtype or not out.is_contiguous() or not out.is_cuda:
         raise ValueError("out must be a contiguous device tensor [..., F] of h's dtype")
-    _check(_lib.load().attn_geglu(h.data_ptr(), out.data_ptr(), rows, F, _DT[h.dtype], _stream()), "attn_geglu")
+    _check(_lib.load().attn_geglu(h.data_ptr(), out.data_ptr(), rows, F, _DT[h.dtype], _stream(h)), "attn_geglu")
     return out
 
 

@@ -580,8 +580,12 @@ const void* coop_kernel(int rv) {
   }
 }
 
+// The one-launch split form tells this call's slice moments from earlier
+// ones by an epoch taken on the host at launch; a captured graph would replay
+// the same epoch over words its previous replay left, so a call on a stream
+// being captured takes the stream-ordered two-launch form instead.
 template <class E>
-GnPlan gn_plan(const GroupNormProblem& p) {
+GnPlan gn_plan(const GroupNormProblem& p, bool capturing) {
   GnPlan pl;
   pl.vec = p.HW % E::VW == 0 && ((uintptr_t)p.x & 15u) == 0 && ((uintptr_t)p.y & 15u) == 0;
   const int VW = pl.vec ? E::VW : 1;
@@ -607,7 +611,7 @@ GnPlan gn_plan(const GroupNormProblem& p) {
   }
   // Split forms: the workspace holds 16 bytes of tagged moments per slice.
   pl.coop_rv = 0;
-  if (forced != 1) {
+  if (forced != 1 && !capturing) {
     // one launch: about kGnSliceTarget workgroups, slices of at most
     // kGnCoopMaxRv vectors per thread, at most kGnCoopMaxSlices per group,
     // all workgroups resident at once
@@ -695,16 +699,26 @@ hipError_t launch_gn_t(const GroupNormProblem& p, const GnPlan& pl) {
   return hipGetLastError();
 }
 
+// Whether work on `st` is being captured into a graph (an error counts as
+// yes: the two-launch form is correct either way).
+bool stream_capturing(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) return true;
+  return cs != hipStreamCaptureStatusNone;
+}
+
 template <class E>
 hipError_t launch_gn_e(const GroupNormProblem& p) {
-  const GnPlan pl = gn_plan<E>(p);
+  const GnPlan pl = gn_plan<E>(p, stream_capturing(p.stream));
   if (pl.ws_bytes > p.workspace_bytes || (pl.ws_bytes && !p.workspace)) return hipErrorInvalidValue;
   return pl.vec ? launch_gn_t<E, true>(p, pl) : launch_gn_t<E, false>(p, pl);
 }
 
+// Enough for the plan of either kind of call, captured or not.
 template <class E>
 size_t gn_ws_e(const GroupNormProblem& p) {
-  return gn_plan<E>(p).ws_bytes;
+  const size_t a = gn_plan<E>(p, false).ws_bytes, b = gn_plan<E>(p, true).ws_bytes;
+  return a > b ? a : b;
 }
 
 // ---------------------------------------------------------------------------

@@ -199,7 +199,11 @@ attn_status attn_scores_pv(const float* a, const float* ml, const void* v, void*
  * with a workspace of attn_group_norm_workspace_size() bytes (device memory,
  * 8-byte aligned, zero-filled before its first use; the kernels leave it
  * ready for the next call of any shape; calls sharing one workspace must not
- * overlap in time); workspace may be NULL when that size is 0.
+ * overlap in time); workspace may be NULL when that size is 0.  A call on a
+ * stream that is being captured into a graph always takes the two-launch
+ * form: the one-launch form tells a call's data in the workspace from an
+ * earlier call's by a tag chosen on the host at launch, which every replay
+ * of a graph would repeat.
  * Requirements: sizes >= 1, C a multiple of G, eps finite and >= 0, pointers
  * aligned to the element size, (C/G)*HW < 2^31, N*C*HW < 2^40; else
  * ATTN_ERR_INVALID_ARG before anything is launched (also for a missing or
@@ -208,9 +212,10 @@ attn_status attn_group_norm(const void* x, const void* gamma, const void* beta, 
                             size_t workspace_bytes, int N, int C, int HW, int G, float eps, attn_dtype dt,
                             void* stream);
 
-/* Workspace bytes attn_group_norm needs for this problem (0: none).  The
- * alignment of x and y enters the plan, so pass the pointers that will be
- * used.  Returns 0 for invalid arguments as well. */
+/* Workspace bytes attn_group_norm needs for this problem (0: none), for a
+ * call on any stream, captured or not.  The alignment of x and y enters the
+ * plan, so pass the pointers that will be used.  Returns 0 for invalid
+ * arguments as well. */
 size_t attn_group_norm_workspace_size(const void* x, const void* y, int N, int C, int HW, int G,
                                       attn_dtype dt);
 

@@ -2,7 +2,10 @@
 every replay, with ordinary eager work and synchronisation between replays,
 must reproduce the eager results bit for bit.  None of the entry points
 records a memset or allocates inside the capture; the group-normalisation
-workspace is sized and allocated by the first (eager) call."""
+workspace is sized and allocated by the first (eager) call.  A captured
+group normalisation takes the two-launch form (the one-launch form's
+call tags would repeat on every replay), so its eager reference is the
+two-launch form too."""
 import pytest
 
 pytestmark = pytest.mark.gpu
@@ -30,15 +33,17 @@ def _work(cfg, q, k, v, x, h, outs):
     attn.geglu(h, out=g)
 
 
-def test_graph_replays_match_eager():
+def test_graph_replays_match_eager(monkeypatch):
     import torch
     cfg, q, k, v, x, h = _inputs()
     mk = lambda: [torch.empty_like(q), torch.empty((2, 8, cfg.Nq, 2), device="cuda"),
                   torch.empty_like(q), torch.empty((2, 8, cfg.Nq, 2), device="cuda"),
                   torch.empty_like(x), torch.empty((2048, 1280), device="cuda", dtype=torch.float16)]
     eager = mk()
+    monkeypatch.setenv("ATTN_GN_PATH", "split")  # the form a captured call takes
     _work(cfg, q, k, v, x, h, eager)
     torch.cuda.synchronize()
+    monkeypatch.delenv("ATTN_GN_PATH")
     outs = mk()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
@@ -51,3 +56,35 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         for i, (a, b) in enumerate(zip(outs, eager)):
             assert torch.equal(a, b), f"replay {rep}: output {i} differs from the eager run"
+
+
+def test_group_norm_graph_on_the_stream_of_earlier_calls():
+    """A graph captured on a stream whose earlier eager group_norm calls
+    allocated the workspace reuses it, unzeroed, on every replay; with new
+    data in x before each replay, every replay must match the eager result
+    for that data (the captured call must not mistake the previous replay's
+    slice moments for its own)."""
+    import torch
+    import attention_attn_stats_amd as attn
+    s = torch.cuda.Stream()
+    g = torch.Generator(device="cuda").manual_seed(21)
+    xs = [(torch.randn((2, 320, 64 * 64), device="cuda", generator=g) * (1 + i) + 0.5 * i).half()
+          for i in range(3)]
+    x, y = torch.empty_like(xs[0]), torch.empty_like(xs[0])
+    with torch.cuda.stream(s):
+        refs = [attn.group_norm(xi, 32, eps=1e-5) for xi in xs]
+        x.copy_(xs[0])
+        attn.group_norm(x, 32, eps=1e-5, out=y)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        attn.group_norm(x, 32, eps=1e-5, out=y)
+    for rep in range(6):
+        i = rep % 3
+        x.copy_(xs[i])
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        err = (y.float() - refs[i].float()).abs().max().item()
+        assert err <= 8e-3, f"replay {rep} (data {i}): max difference {err} from the eager result"
