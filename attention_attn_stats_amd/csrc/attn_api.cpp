@@ -78,6 +78,14 @@ attn_status run_pf(const Problem& p) {
   return s == ATTN_OK ? run_pv(p) : s;
 }
 
+// Whether work on `st` is being captured into a graph (an error counts as
+// yes: then nothing synchronises).
+bool stream_capturing(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) return true;
+  return cs != hipStreamCaptureStatusNone;
+}
+
 // ---- variant cache -------------------------------------------------------
 typedef std::tuple<int, int, int, int, int, int> Key;  // BH, Nq, Nk, d, dtype, device
 std::mutex g_mu;
@@ -254,6 +262,11 @@ attn_status attn_forward_strided(const void* q, const void* k, const void* v, vo
       std::lock_guard<std::mutex> g(g_mu);
       auto it = g_cache.find(key);
       if (it != g_cache.end()) var = it->second;
+    }
+    if (var == ATTN_AUTO && stream_capturing(p.stream)) {
+      // timing synchronises, which a stream being captured into a graph
+      // must not do: the rule-of-thumb choice, not cached
+      var = attn_default_variant(p.d);
     }
     if (var == ATTN_AUTO) {
       attn_variant chosen = ATTN_AUTO;

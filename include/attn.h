@@ -112,7 +112,9 @@ attn_status attn_flash(const void* q, const void* k, const void* v, void* out, f
  * (call attn_flash with ml_out to get them); ATTN_AUTO uses the cached choice for this
  * shape, and on the first call for a shape times both variants on the
  * caller's buffers (synchronising `stream` once) before caching the winner
- * (if `ml` is NULL only FLASH is eligible).  The environment variable
+ * (if `ml` is NULL only FLASH is eligible); on a stream being captured into
+ * a graph a shape not yet timed takes attn_default_variant(d) instead,
+ * uncached, as nothing may synchronise there.  The environment variable
  * ATTN_VARIANT=pf|flash overrides ATTN_AUTO. */
 attn_status attn_forward(const void* q, const void* k, const void* v, void* out, float* ml,
                          int B, int H, int Nq, int Nk, int d, float scale, attn_variant var,

@@ -88,3 +88,31 @@ def test_group_norm_graph_on_the_stream_of_earlier_calls():
         torch.cuda.synchronize()
         err = (y.float() - refs[i].float()).abs().max().item()
         assert err <= 8e-3, f"replay {rep} (data {i}): max difference {err} from the eager result"
+
+
+def test_auto_forward_captured_for_an_untimed_shape():
+    """ATTN_AUTO on a shape not yet timed, inside a capture: nothing may
+    synchronise there, so the call takes the default variant (the two-pass
+    form at d = 80) and the replay reproduces it bit for bit."""
+    import torch
+    import attention_attn_stats_amd as attn
+    attn.select_reset()
+    g = torch.Generator(device="cuda").manual_seed(22)
+    q, k, v = (torch.randn((1, 2, 300, 80), device="cuda", generator=g).half() for _ in range(3))
+    out = torch.empty_like(q)
+    ml = torch.empty((1, 2, 300, 2), device="cuda")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        attn.forward(q, k, v, variant="auto", out=out, ml=ml)
+    out.fill_(float("nan"))
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    ml_ref = attn.stats(q, k)
+    o_ref = attn.pv(q, k, v, ml_ref)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o_ref) and torch.equal(ml, ml_ref)
+    # the shape was not cached by the captured call: an eager call times it now
+    o2, _ = attn.forward(q, k, v, variant="auto")
+    torch.cuda.synchronize()
+    assert (o2.float() - o_ref.float()).abs().max().item() <= 5e-3
