@@ -454,6 +454,8 @@ attn_variant attn_select(int B, int H, int Nq, int Nk, int d, attn_dtype dt, voi
     auto it = g_cache.find(key);
     if (it != g_cache.end()) return it->second;
   }
+  // timing allocates and synchronises: not on a stream being captured
+  if (stream_capturing(p.stream)) return attn_default_variant(d);
   const size_t esz = dt == ATTN_F32 ? 4 : 2;
   const size_t nq = (size_t)p.BH * Nq * d * esz, nk = (size_t)p.BH * Nk * d * esz;
   void *bq = nullptr, *bk = nullptr, *bv = nullptr, *bo = nullptr, *bml = nullptr;

@@ -233,7 +233,9 @@ attn_status attn_geglu(const void* h, void* out, int rows, int F, attn_dtype dt,
 /* The variant ATTN_AUTO uses for this shape.  On a cache miss it allocates
  * temporary device buffers, times both variants on `stream`, frees the
  * buffers and caches the winner, so it synchronises and may allocate; call it
- * outside timed or captured regions.  Returns ATTN_AUTO (0) on error. */
+ * outside timed regions.  On a stream being captured into a graph a cache
+ * miss returns attn_default_variant(d) without timing or caching.  Returns
+ * ATTN_AUTO (0) on error. */
 attn_variant attn_select(int B, int H, int Nq, int Nk, int d, attn_dtype dt, void* stream);
 
 /* Before any measurement the choice follows the write-up's own rule: the

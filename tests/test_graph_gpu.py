@@ -103,7 +103,9 @@ def test_auto_forward_captured_for_an_untimed_shape():
     ml = torch.empty((1, 2, 300, 2), device="cuda")
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
+        chosen = attn.select(1, 2, 300, 300, 80)  # no timing inside the capture either
         attn.forward(q, k, v, variant="auto", out=out, ml=ml)
+    assert chosen == "pf"
     out.fill_(float("nan"))
     torch.cuda.synchronize()
     graph.replay()
