@@ -12,6 +12,7 @@ tensors' own strides, without a copy.
 """
 from __future__ import annotations
 
+import collections
 import math
 
 import torch
@@ -227,18 +228,25 @@ def scores_pv(a, ml, v, out=None):
     return out
 
 
-_GN_WS = {}
+_GN_WS: "collections.OrderedDict" = collections.OrderedDict()
+_GN_WS_MAX = 16  # streams with a cached workspace (least recently used dropped first)
 
 
 def _gn_workspace(device, nbytes: int) -> torch.Tensor:
     """A group-normalisation workspace of at least nbytes, one per device and
-    stream (kernels on one stream never overlap, so they may share it)."""
+    stream (kernels on one stream never overlap, so they may share it).  A
+    workspace is allocated while its stream is current and used on that
+    stream only, so dropping it from the cache is ordered after its last use
+    by the allocator."""
     key = (device, _raw_stream(device.index) if _raw_stream is not None
            else torch.cuda.current_stream(device).cuda_stream)
     ws = _GN_WS.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)  # zero-filled before first use
         _GN_WS[key] = ws
+        while len(_GN_WS) > _GN_WS_MAX:
+            _GN_WS.popitem(last=False)
+    _GN_WS.move_to_end(key)
     return ws
 
 

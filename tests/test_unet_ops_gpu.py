@@ -289,3 +289,22 @@ def test_geglu_unaligned_and_odd_sizes():
     _geglu_case(9, 640, "bf16", seed=6, offset_elems=5)
     with pytest.raises(ValueError):
         attn.geglu(torch.zeros(4, 7, device="cuda", dtype=torch.float16))  # odd last dim
+
+
+def test_group_norm_workspace_cache_is_bounded():
+    # a workspace per stream, the least recently used dropped beyond the bound;
+    # every call still matches the oracle
+    import torch
+    import attention_attn_stats_amd as attn
+    from attention_attn_stats_amd import api
+    x = torch.randn((2, 320, 64 * 64), device="cuda", generator=torch.Generator(device="cuda").manual_seed(4)).half()
+    ref = attn.group_norm(x, 32)
+    for _ in range(api._GN_WS_MAX + 5):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            y = attn.group_norm(x, 32)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref)
+    assert len(api._GN_WS) <= api._GN_WS_MAX
