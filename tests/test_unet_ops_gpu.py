@@ -308,3 +308,37 @@ def test_group_norm_workspace_cache_is_bounded():
         torch.cuda.synchronize()
         assert torch.equal(y, ref)
     assert len(api._GN_WS) <= api._GN_WS_MAX
+
+
+def _random_gn_cases(n=30, seed=20261204):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        G = int(rng.choice([1, 2, 8, 32]))
+        C = G * int(rng.integers(1, 41))
+        HW = int(rng.integers(1, 9000)) if i % 3 else int(rng.choice([64, 256, 1024, 4096]))
+        N = int(rng.integers(1, 4))
+        dtype = ("f16", "bf16", "f32")[i % 3]
+        out.append((N, C, HW, G, dtype))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_gn_cases(), ids=lambda c: "x".join(map(str, c[:4])) + f"-{c[4]}")
+def test_group_norm_random_shapes(case):
+    # seeded random shapes: groups from a handful of elements to ~360000,
+    # aligned and ragged spatial sizes, every element type; the plan picks
+    # whichever form fits, each checked against the oracle's bound
+    N, C, HW, G, dtype = case
+    _gn_case(N, C, HW, G, dtype, seed=N * 7919 + C * 104729 + HW * 13 + G)
+
+
+def _random_geglu_cases(n=20, seed=20261205):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 3000)), int(rng.integers(1, 3000)), ("f16", "bf16", "f32")[i % 3])
+            for i in range(n)]
+
+
+@pytest.mark.parametrize("case", _random_geglu_cases(), ids=lambda c: f"{c[0]}x{c[1]}-{c[2]}")
+def test_geglu_random_shapes(case):
+    rows, F, dtype = case
+    _geglu_case(rows, F, dtype, seed=rows * 31 + F)
