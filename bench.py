@@ -378,7 +378,7 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(cfg, budget_s: float = 15.0):
+def cpu_baseline(cfg, budget_s: float = 20.0):
     """The float64 oracle timed on a bounded sample of the workload: whole
     heads (all Nq query rows against all Nk keys), as many passes over the
     heads as fill about `budget_s` seconds of wall time."""
