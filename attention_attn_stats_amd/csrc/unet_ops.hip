@@ -93,9 +93,10 @@ struct EF32 {
 //    across the workgroup and writes the group from registers.  Used when
 //    the groups fill the chip or are small.
 //  - gn_coop_kernel: S workgroups per group, each holding its slice in
-//    registers, exchange slice moments through a small workspace at a
-//    per-group arrival counter (bounded wait, see there) -- one launch for
-//    the few large groups of a batch-2 UNet.
+//    registers, exchange slice moments through a small workspace as words
+//    tagged with the call's epoch (bounded wait, see there) -- one launch for
+//    the few large groups of a batch-2 UNet; not used on a stream being
+//    captured into a graph, whose replays would repeat the epoch.
 //  - gn_partial_kernel + gn_apply_kernel: two launches over S slices (the
 //    first writes each slice's moments, the second merges its group's
 //    moments in slice order and normalises its slice, reading x again), for
