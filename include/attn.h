@@ -57,6 +57,8 @@
 #ifndef ATTN_H
 #define ATTN_H
 
+#include <stddef.h> /* size_t */
+
 #ifdef __cplusplus
 extern "C" {
 #endif

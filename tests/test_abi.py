@@ -28,6 +28,28 @@ def test_header_and_binding_agree():
     assert set(_declared()) == set(_lib.EXPORTS)
 
 
+@pytest.mark.parametrize("lang,std", [("c", "-std=c99"), ("c++", "-std=c++11")])
+def test_header_is_plain_c_and_cxx(tmp_path, lang, std):
+    # includable without HIP headers, from C and C++, warning-free; a C
+    # program linking against the library resolves every entry point
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc" if lang == "c" else "g++")
+    if cc is None:
+        pytest.skip("no host compiler")
+    src = tmp_path / ("use.c" if lang == "c" else "use.cpp")
+    calls = "\n".join(f"  (void)&{n};" for n in _declared())
+    src.write_text('#include "attn.h"\nint main(void) {\n' + calls + '\n  return attn_status_string(ATTN_OK) == 0;\n}\n')
+    cmd = [cc, std, "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"), str(src), "-o",
+           str(tmp_path / "use")]
+    if os.path.exists(_lib.LIB_PATH):
+        cmd += [_lib.LIB_PATH]
+    else:
+        cmd = cmd[:-2] + ["-fsyntax-only"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
 def test_every_declared_symbol_is_exported(lib):
     for name in _declared():
         assert hasattr(lib, name), name
