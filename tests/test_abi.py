@@ -213,3 +213,12 @@ def test_group_norm_and_geglu_validation(lib):
     assert ge(P + 1, P, 4, 8, f, None) == _lib.ERR_INVALID_ARG
     assert ge(P, P, 1 << 16, 1 << 15, f, None) == _lib.ERR_INVALID_ARG  # rows * F >= 2^31 - 512
     assert ge(P, P, 4, 8, 9, None) == _lib.ERR_UNSUPPORTED
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    # no fallback: without libattn.so every entry point raises, naming the
+    # build command
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libattn.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError, match="attention_attn_stats_amd.build"):
+        _lib.load()
