@@ -5,6 +5,7 @@ use and the faster is cached.  These tests check the mechanics: the choice is
 one of the two forms, cached per shape, overridden by ATTN_VARIANT, forgotten
 by attn_select_reset, and an ATTN_AUTO forward that times a new shape leaves
 exactly the chosen form's output (bit for bit)."""
+import numpy as np
 import pytest
 
 from attention_attn_stats_amd.configs import CONFIGS
@@ -53,3 +54,49 @@ def test_auto_forward_leaves_the_chosen_forms_output(name, monkeypatch):
     o2, _ = attn.forward(q, k, v, variant="auto", scale=cfg.scale)
     torch.cuda.synchronize()
     assert torch.equal(o2, ref)
+
+
+def test_concurrent_callers(monkeypatch):
+    """Four host threads, each on its own stream, call ATTN_AUTO on shapes not
+    yet timed (two threads share one shape, so they race on its cache entry):
+    every result matches the oracle, and the cache ends with one choice per
+    shape."""
+    import threading
+    import torch
+    import attention_attn_stats_amd as attn
+    from attention_attn_stats_amd import synth
+    from gpu_util import assert_close_o, from_device, reference
+    monkeypatch.delenv("ATTN_VARIANT", raising=False)
+    attn.select_reset()
+    shapes = [(1, 2, 300, 257, 40), (1, 2, 200, 129, 80), (1, 1, 96, 65, 160), (1, 2, 300, 257, 40)]
+    data = []
+    for i, (B, H, Nq, Nk, d) in enumerate(shapes):
+        q = synth.tensor(500 + i, (B, H, Nq, d), "f16")
+        k = synth.tensor(600 + i, (B, H, Nk, d), "f16")
+        v = synth.tensor(700 + i, (B, H, Nk, d), "f16")
+        data.append((q, k, v, float(np.float32(1 / np.sqrt(d)))))
+    outs, errs = [None] * len(shapes), []
+
+    def work(i):
+        try:
+            q, k, v, scale = data[i]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                tq, tk, tv = (to_device(x, "f16") for x in (q, k, v))
+                o, _ = attn.forward(tq, tk, tv, variant="auto", scale=scale)
+                s.synchronize()
+                outs[i] = from_device(o)
+        except Exception as e:  # reported below
+            errs.append(repr(e))
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(shapes))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errs, errs
+    for i, (q, k, v, scale) in enumerate(data):
+        o_ref, _ = reference(q, k, v, "f16", scale)
+        assert_close_o(outs[i], o_ref, "f16", f"thread {i} {shapes[i]}")
+    for B, H, Nq, Nk, d in shapes:
+        assert attn.select(B, H, Nq, Nk, d) in ("pf", "flash")
