@@ -612,7 +612,9 @@ GnPlan gn_plan(const GroupNormProblem& p, bool capturing) {
   }
   // Split forms: the workspace holds 16 bytes of tagged moments per slice.
   pl.coop_rv = 0;
-  if (forced != 1 && !capturing) {
+  // not in place either: a workgroup whose wait runs out recomputes its
+  // partners' moments from x, which an in-place partner may have overwritten
+  if (forced != 1 && !capturing && p.x != p.y) {
     // one launch: about kGnSliceTarget workgroups, slices of at most
     // kGnCoopMaxRv vectors per thread, at most kGnCoopMaxSlices per group,
     // all workgroups resident at once

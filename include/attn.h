@@ -204,10 +204,11 @@ attn_status attn_scores_pv(const float* a, const float* ml, const void* v, void*
  * 8-byte aligned, zero-filled before its first use; the kernels leave it
  * ready for the next call of any shape; calls sharing one workspace must not
  * overlap in time); workspace may be NULL when that size is 0.  A call on a
- * stream that is being captured into a graph always takes the two-launch
- * form: the one-launch form tells a call's data in the workspace from an
- * earlier call's by a tag chosen on the host at launch, which every replay
- * of a graph would repeat.
+ * stream that is being captured into a graph, or in place (y == x), takes the
+ * two-launch form instead of the one-launch split: the latter tells a call's
+ * data in the workspace from an earlier call's by a tag chosen on the host
+ * at launch, which every replay of a graph would repeat, and its bounded
+ * wait falls back to reading its partners' slices of x.
  * Requirements: sizes >= 1, C a multiple of G, eps finite and >= 0, pointers
  * aligned to the element size, (C/G)*HW < 2^31, N*C*HW < 2^40; else
  * ATTN_ERR_INVALID_ARG before anything is launched (also for a missing or

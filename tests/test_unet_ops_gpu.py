@@ -342,3 +342,14 @@ def _random_geglu_cases(n=20, seed=20261205):
 def test_geglu_random_shapes(case):
     rows, F, dtype = case
     _geglu_case(rows, F, dtype, seed=rows * 31 + F)
+
+
+@pytest.mark.parametrize("C,HW", [(320, 4096), (960, 4096)], ids=lambda v: str(v))
+def test_group_norm_in_place_with_no_wait(C, HW, monkeypatch):
+    # in place, with the one-launch split form asked for and no polls
+    # allowed: an in-place call must not take a form whose fallback rereads
+    # its partners' slices of x (which they may already have overwritten)
+    monkeypatch.setenv("ATTN_GN_PATH", "coop")
+    monkeypatch.setenv("ATTN_GN_SPIN", "0")
+    for dtype in ("f16", "bf16"):
+        _gn_case(2, C, HW, 32, dtype, seed=C + HW + 7, inplace=True)
