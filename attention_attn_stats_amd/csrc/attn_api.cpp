@@ -86,6 +86,26 @@ bool stream_capturing(hipStream_t st) {
   return cs != hipStreamCaptureStatusNone;
 }
 
+// Byte range [first, last] a [B][H][N][d] tensor of the problem spans.
+struct Span {
+  uintptr_t first, last;
+};
+Span span_of(const void* p, const attn::Strides& s, int B, int H, int N, int d, size_t esz) {
+  const long long last = (long long)(B - 1) * s.batch + (long long)(H - 1) * s.head + (long long)(N - 1) * s.row + d;
+  return Span{(uintptr_t)p, (uintptr_t)p + (uintptr_t)(last * (long long)esz) - 1};
+}
+bool overlap(const Span& a, const Span& b) { return a.first <= b.last && b.first <= a.last; }
+// Whether out's memory range meets that of q, k or v (timing would then run
+// a form over its own output).
+bool out_meets_inputs(const Problem& p) {
+  const size_t esz = p.dt == ATTN_F32 ? 4 : 2;
+  const int B = p.BH / p.lay.H, H = p.lay.H;
+  const Span o = span_of(p.out, p.lay.o, B, H, p.Nq, p.d, esz);
+  return overlap(o, span_of(p.q, p.lay.q, B, H, p.Nq, p.d, esz)) ||
+         overlap(o, span_of(p.k, p.lay.k, B, H, p.Nk, p.d, esz)) ||
+         overlap(o, span_of(p.v, p.lay.v, B, H, p.Nk, p.d, esz));
+}
+
 // ---- variant cache -------------------------------------------------------
 typedef std::tuple<int, int, int, int, int, int> Key;  // BH, Nq, Nk, d, dtype, device
 std::mutex g_mu;
@@ -263,9 +283,11 @@ attn_status attn_forward_strided(const void* q, const void* k, const void* v, vo
       auto it = g_cache.find(key);
       if (it != g_cache.end()) var = it->second;
     }
-    if (var == ATTN_AUTO && stream_capturing(p.stream)) {
+    if (var == ATTN_AUTO && (stream_capturing(p.stream) || out_meets_inputs(p))) {
       // timing synchronises, which a stream being captured into a graph
-      // must not do: the rule-of-thumb choice, not cached
+      // must not do, and runs both forms several times, which an output
+      // sharing memory with an input would corrupt: the rule-of-thumb
+      // choice, not cached
       var = attn_default_variant(p.d);
     }
     if (var == ATTN_AUTO) {

@@ -46,7 +46,9 @@
  * Supported: d in {40, 80, 160}; dt in {ATTN_F32, ATTN_F16, ATTN_BF16};
  * any B, H, Nq, Nk >= 1 with B*H*max(Nq,Nk)*d < 2^31 elements per tensor;
  * scale finite and > 0 (the usual 1/sqrt(d) softmax temperature).  q, k, v,
- * out must be 16-byte aligned and ml 8-byte aligned.
+ * out must be 16-byte aligned and ml 8-byte aligned.  out may be q itself (each
+ * query row is read before its output row is written, by the same workgroup)
+ * but must not share memory with k or v, which every workgroup of a head reads.
  * F16/BF16 run on the matrix cores with float32 accumulation and float32
  * softmax state; F32 is a vector-ALU float32 path kept for exactness checks.
  *
@@ -115,8 +117,10 @@ attn_status attn_flash(const void* q, const void* k, const void* v, void* out, f
  * shape, and on the first call for a shape times both variants on the
  * caller's buffers (synchronising `stream` once) before caching the winner
  * (if `ml` is NULL only FLASH is eligible); on a stream being captured into
- * a graph a shape not yet timed takes attn_default_variant(d) instead,
- * uncached, as nothing may synchronise there.  The environment variable
+ * a graph, or when `out` shares memory with q, k or v (in place over q, say),
+ * a shape not yet timed takes attn_default_variant(d) instead, uncached, as
+ * nothing may synchronise in a capture and repeated runs would read their
+ * own output.  The environment variable
  * ATTN_VARIANT=pf|flash overrides ATTN_AUTO. */
 attn_status attn_forward(const void* q, const void* k, const void* v, void* out, float* ml,
                          int B, int H, int Nq, int Nk, int d, float scale, attn_variant var,

@@ -100,3 +100,32 @@ def test_concurrent_callers(monkeypatch):
         assert_close_o(outs[i], o_ref, "f16", f"thread {i} {shapes[i]}")
     for B, H, Nq, Nk, d in shapes:
         assert attn.select(B, H, Nq, Nk, d) in ("pf", "flash")
+
+
+def test_auto_forward_in_place_over_q(monkeypatch):
+    """out = q: an untimed shape must not be timed (repeated runs would read
+    their own output); the default variant runs once, and the result equals
+    the out-of-place one bit for bit."""
+    import torch
+    import attention_attn_stats_amd as attn
+    from attention_attn_stats_amd import synth
+    monkeypatch.delenv("ATTN_VARIANT", raising=False)
+    q = synth.tensor(801, (1, 2, 300, 80), "f16")
+    k = synth.tensor(802, (1, 2, 333, 80), "f16")
+    v = synth.tensor(803, (1, 2, 333, 80), "f16")
+    scale = float(np.float32(1 / np.sqrt(80)))
+    tq, tk, tv = (to_device(x, "f16") for x in (q, k, v))
+    ml = attn.stats(tq, tk, scale=scale)
+    ref = attn.pv(tq, tk, tv, ml, scale=scale)  # the default variant at d = 80
+    attn.select_reset()
+    inplace = tq.clone()
+    attn.forward(inplace, tk, tv, variant="auto", out=inplace, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(inplace, ref)
+    for form in ("flash", "pf"):  # the explicit forms in place over q as well
+        inplace = tq.clone()
+        attn.forward(inplace, tk, tv, variant=form, out=inplace, scale=scale)
+        torch.cuda.synchronize()
+        expect = ref if form == "pf" else attn.flash(tq, tk, tv, scale=scale)
+        torch.cuda.synchronize()
+        assert torch.equal(inplace, expect), form
