@@ -30,6 +30,14 @@ HIPCC_FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 
+# Flags of one source only.  The attention kernels take the scheduler's
+# iterative ILP strategy: the same instructions, ordered for more latency
+# hiding; measured -10 % at 256 queries x d = 160, neutral at 4096 x d = 40,
+# bit-identical results.
+FILE_FLAGS = {
+    "attn_mfma.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
+
 
 _MFMA_OP = re.compile(r"^\s*(v_mfma_\S+)")
 # MFMA opcodes whose VGPR-form code (accumulator in ordinary VGPRs, chains
@@ -69,7 +77,8 @@ def verify_device_code(hipcc: str, verbose: bool = False, defines=()) -> None:
     for src in MFMA_SOURCES:
         with tempfile.TemporaryDirectory() as td:
             asm = os.path.join(td, src + ".s")
-            cmd = [hipcc, *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-x", "hip", "--cuda-device-only", "-S",
+            cmd = [hipcc, *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), *[f"-D{d}" for d in defines],
+                   "-x", "hip", "--cuda-device-only", "-S",
                    os.path.join(CSRC, src), "-o", asm]
             r = subprocess.run(cmd, capture_output=True, text=True)
             if r.returncode != 0:
@@ -93,7 +102,7 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     for src in SOURCES:
         obj = os.path.join(objdir, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
-        cmd = [hipcc, *HIPCC_FLAGS, *[f"-D{d}" for d in defines], *lang, "-c",
+        cmd = [hipcc, *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), *[f"-D{d}" for d in defines], *lang, "-c",
                os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

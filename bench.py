@@ -42,14 +42,20 @@ def log(*a):
 
 
 def kernel_hash() -> str:
-    """Hash of the kernel source without its comments and blank space, so
-    that a comment edit does not orphan counters taken on the same code."""
+    """Hash of the kernel source without its comments and blank space, and
+    of the compile flags of that file alone, so that a comment edit does not
+    orphan counters taken on the same code but a flag that changes the code
+    does."""
     import re
+    from attention_attn_stats_amd import build as _build
     with open(KERNEL_SRC) as f:
         src = f.read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     src = re.sub(r"//[^\n]*", "", src)
     src = "\n".join(ln.strip() for ln in src.splitlines() if ln.strip())
+    flags = _build.FILE_FLAGS.get(os.path.basename(KERNEL_SRC), [])
+    if flags:
+        src += "\n#flags " + " ".join(flags)
     return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 

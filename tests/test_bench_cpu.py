@@ -3,7 +3,7 @@ algorithmic work it divides by (checked against the per-config figures of the
 workload table, worked out by hand from the shapes: FLOP = 4 B H Nq Nk d; flash
 bytes = Q + K + V + O; two-pass bytes = 2Q + 2K + V + O + 2 ml; stats-pass bytes
 = Q + K + ml, 2-byte elements and 8-byte (m, l) rows), and the rule that stored
-traffic counters are reported only for the kernel source they were taken on."""
+traffic counters are reported only for the kernel source and flags they were taken on."""
 import json
 import os
 import subprocess
@@ -65,3 +65,8 @@ def test_traffic_is_reported_only_for_the_profiled_source(tmp_path, monkeypatch)
     src.write_text("int f() {\n  return 2;\n}\n")
     assert bench.kernel_hash() != h and bench.load_traffic("attn_flash", "sd512_self") is None
     assert bench.load_traffic("attn_flash", "other_workload") is None
+    # ... and so do compile flags given to that file alone
+    from attention_attn_stats_amd import build
+    h2 = bench.kernel_hash()
+    monkeypatch.setitem(build.FILE_FLAGS, "kernel.hip", ["-mllvm", "-some-option"])
+    assert bench.kernel_hash() != h2
