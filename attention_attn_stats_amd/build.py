@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libattn.so")
-SOURCES = ["attn_api.cpp", "attn_mfma.hip", "attn_f32.hip", "attn_scores.hip", "unet_ops.hip"]
+SOURCES = ["attn_api.cpp", "attn_mfma.hip", "attn_fa40.hip", "attn_f32.hip", "attn_scores.hip", "unet_ops.hip"]
 ARCH = os.environ.get("ATTN_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
@@ -68,7 +68,7 @@ def unverified_mfma(asm_text: str) -> list:
     return bad
 
 
-MFMA_SOURCES = ["attn_mfma.hip", "attn_scores.hip"]
+MFMA_SOURCES = ["attn_mfma.hip", "attn_fa40.hip", "attn_scores.hip"]
 
 
 def verify_device_code(hipcc: str, verbose: bool = False, defines=()) -> None:

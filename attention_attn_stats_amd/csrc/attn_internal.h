@@ -52,6 +52,10 @@ struct Problem {
 hipError_t launch_mfma_stats(const Problem& p);
 hipError_t launch_mfma_pv(const Problem& p);
 hipError_t launch_mfma_flash(const Problem& p);  // writes p.ml when it is non-null
+// The software-pipelined head-dimension-40 kernels (fp16 / bf16, dense or
+// strided); `cus` = compute units of the device.
+hipError_t launch_fa40_flash(const Problem& p, int cus);  // writes p.ml when it is non-null
+hipError_t launch_fa40_pv(const Problem& p, int cus);
 
 // The partially fused form over a stored logit matrix A (float32).
 hipError_t launch_scores(const Problem& p, float* a);                   // A = scale Q K^T
