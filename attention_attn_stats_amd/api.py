@@ -45,10 +45,17 @@ def _dims(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None):
     dt = q.dtype
     if dt not in _DT:
         raise ValueError(f"unsupported dtype {dt}")
+    dev = q.device
     for t in (q, k, v):
-        if t is not None and (not t.is_cuda or t.dtype != dt or (d > 1 and t.stride(3) != 1)):
-            raise ValueError("q, k, v must be device tensors of one dtype with contiguous rows")
+        if t is not None and (not t.is_cuda or t.dtype != dt or (d > 1 and t.stride(3) != 1) or t.device != dev):
+            raise ValueError("q, k, v must be tensors on one device, of one dtype, with contiguous rows")
     return B, H, Nq, Nk, d
+
+
+def _check_ml(ml, shape, device):
+    if (ml.shape != shape or ml.dtype != torch.float32 or not ml.is_contiguous() or not ml.is_cuda
+            or ml.device != device):
+        raise ValueError(f"ml must be a contiguous float32 {list(shape)} tensor on {device}")
 
 
 def _strides(t: torch.Tensor) -> _lib.Strides:
@@ -73,8 +80,9 @@ def _layout(q, k, v=None, out=None):
 def _out_for(q, out):
     if out is None:
         return torch.empty_like(q)  # keeps q's strides when q is a dense view
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_cuda or out.stride(3) != 1:
-        raise ValueError("out must be a device tensor of q's shape and dtype with contiguous rows")
+    if (out.shape != q.shape or out.dtype != q.dtype or not out.is_cuda or out.stride(3) != 1
+            or out.device != q.device):
+        raise ValueError("out must be a tensor on q's device, of q's shape and dtype, with contiguous rows")
     # (a contiguous tensor cannot overlap itself)
     if not out.is_contiguous() and torch._debug_has_internal_overlap(out) == 1:
         raise ValueError("out must not have overlapping elements")
@@ -106,8 +114,7 @@ def _ml_for(q, ml):
     B, H, Nq, _ = q.shape
     if ml is None:
         return torch.empty((B, H, Nq, 2), device=q.device, dtype=torch.float32)
-    if ml.shape != (B, H, Nq, 2) or ml.dtype != torch.float32 or not ml.is_contiguous() or not ml.is_cuda:
-        raise ValueError("ml must be a contiguous float32 [B, H, Nq, 2] device tensor")
+    _check_ml(ml, (B, H, Nq, 2), q.device)
     return ml
 
 
@@ -128,8 +135,7 @@ def stats(q, k, ml=None, scale=None):
 def pv(q, k, v, ml, out=None, scale=None):
     """O = softmax(A) v from statistics produced by stats()."""
     B, H, Nq, Nk, d = _dims(q, k, v)
-    if ml.shape != (B, H, Nq, 2) or ml.dtype != torch.float32 or not ml.is_contiguous():
-        raise ValueError("ml must be a contiguous float32 [B, H, Nq, 2] device tensor")
+    _check_ml(ml, (B, H, Nq, 2), q.device)
     out = _out_for(q, out)
     lay = _layout(q, k, v, out)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), ml.data_ptr(), out.data_ptr())
@@ -178,8 +184,9 @@ def forward(q, k, v, variant="auto", out=None, ml=None, scale=None):
 def _a_for(B, H, Nq, Nk, device, a):
     if a is None:
         return torch.empty((B, H, Nq, Nk), device=device, dtype=torch.float32)
-    if a.shape != (B, H, Nq, Nk) or a.dtype != torch.float32 or not a.is_contiguous() or not a.is_cuda:
-        raise ValueError("a must be a contiguous float32 [B, H, Nq, Nk] device tensor")
+    if (a.shape != (B, H, Nq, Nk) or a.dtype != torch.float32 or not a.is_contiguous() or not a.is_cuda
+            or a.device != device):
+        raise ValueError(f"a must be a contiguous float32 [B, H, Nq, Nk] tensor on {device}")
     return a
 
 
@@ -201,8 +208,8 @@ def scores_stats(a, ml=None):
     B, H, Nq, Nk = a.shape
     if ml is None:
         ml = torch.empty((B, H, Nq, 2), device=a.device, dtype=torch.float32)
-    elif ml.shape != (B, H, Nq, 2) or ml.dtype != torch.float32 or not ml.is_contiguous() or not ml.is_cuda:
-        raise ValueError("ml must be a contiguous float32 [B, H, Nq, 2] device tensor")
+    else:
+        _check_ml(ml, (B, H, Nq, 2), a.device)
     _check(_lib.load().attn_scores_stats(a.data_ptr(), ml.data_ptr(), B, H, Nq, Nk, _stream(a)),
            "attn_scores_stats")
     return ml
@@ -213,16 +220,17 @@ def scores_pv(a, ml, v, out=None):
     if a.dim() != 4 or a.dtype != torch.float32 or not a.is_cuda or not a.is_contiguous():
         raise ValueError("a must be a contiguous float32 [B, H, Nq, Nk] device tensor")
     B, H, Nq, Nk = a.shape
-    if v.dim() != 4 or tuple(v.shape[:3]) != (B, H, Nk) or not v.is_cuda or not v.is_contiguous():
-        raise ValueError(f"v shape {tuple(v.shape)} does not match a {tuple(a.shape)}")
+    if (v.dim() != 4 or tuple(v.shape[:3]) != (B, H, Nk) or not v.is_cuda or not v.is_contiguous()
+            or v.device != a.device):
+        raise ValueError(f"v {tuple(v.shape)} must be a contiguous tensor on a's device matching a {tuple(a.shape)}")
     if v.dtype not in _DT:
         raise ValueError(f"unsupported dtype {v.dtype}")
-    if ml.shape != (B, H, Nq, 2) or ml.dtype != torch.float32 or not ml.is_contiguous():
-        raise ValueError("ml must be a contiguous float32 [B, H, Nq, 2] device tensor")
+    _check_ml(ml, (B, H, Nq, 2), a.device)
     d = v.shape[3]
     out = torch.empty((B, H, Nq, d), device=v.device, dtype=v.dtype) if out is None else out
-    if out.shape != (B, H, Nq, d) or out.dtype != v.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [B, H, Nq, d] tensor of v's dtype")
+    if (out.shape != (B, H, Nq, d) or out.dtype != v.dtype or not out.is_contiguous() or not out.is_cuda
+            or out.device != a.device):
+        raise ValueError("out must be a contiguous [B, H, Nq, d] tensor of v's dtype on a's device")
     _check(_lib.load().attn_scores_pv(a.data_ptr(), ml.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, Nq, Nk,
                                       d, _DT[v.dtype], _stream(a)), "attn_scores_pv")
     return out
