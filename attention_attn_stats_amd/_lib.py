@@ -19,7 +19,8 @@ EXPORTS = ("attn_stats", "attn_pv", "attn_flash", "attn_forward", "attn_select",
            "attn_default_variant", "attn_select_reset", "attn_status_string",
            "attn_scores", "attn_scores_stats", "attn_scores_pv",
            "attn_stats_strided", "attn_pv_strided", "attn_flash_strided", "attn_forward_strided",
-           "attn_group_norm", "attn_group_norm_workspace_size", "attn_geglu")
+           "attn_group_norm", "attn_group_norm_workspace_size", "attn_geglu",
+           "attn_group_norm_static")
 
 _lib = None
 
@@ -87,6 +88,8 @@ def load() -> ctypes.CDLL:
     lib.attn_forward_strided.restype = _i
     lib.attn_group_norm.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _i, _i, _i, _i, _f, _i, _vp]
     lib.attn_group_norm.restype = _i
+    lib.attn_group_norm_static.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp]
+    lib.attn_group_norm_static.restype = _i
     lib.attn_group_norm_workspace_size.argtypes = [_vp, _vp, _i, _i, _i, _i, _i]
     lib.attn_group_norm_workspace_size.restype = ctypes.c_size_t
     lib.attn_geglu.argtypes = [_vp, _vp, _i, _i, _i, _vp]

@@ -441,6 +441,22 @@ attn_status attn_group_norm(const void* x, const void* gamma, const void* beta, 
   return to_status(attn::launch_group_norm(p));
 }
 
+attn_status attn_group_norm_static(const void* x, const void* gamma, const void* beta, void* y, int N, int C,
+                                   int HW, int G, float eps, attn_dtype dt, void* stream) {
+  attn::GroupNormProblem p;
+  attn_status s = gn_problem(x, gamma, beta, y, N, C, HW, G, eps, dt, stream, &p);
+  if (s != ATTN_OK) return s;
+  const size_t need = attn::group_norm_workspace(p);
+  if (need > attn::kGnStaticScratchBytes) return ATTN_ERR_INVALID_ARG;
+  if (need) {
+    void* ws = nullptr;
+    if (attn::group_norm_static_scratch(&ws) != hipSuccess) return ATTN_ERR_HIP;
+    p.workspace = ws;
+    p.workspace_bytes = attn::kGnStaticScratchBytes;
+  }
+  return to_status(attn::launch_group_norm(p));
+}
+
 size_t attn_group_norm_workspace_size(const void* x, const void* y, int N, int C, int HW, int G,
                                       attn_dtype dt) {
   attn::GroupNormProblem p;

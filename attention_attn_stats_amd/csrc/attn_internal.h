@@ -78,6 +78,10 @@ struct GroupNormProblem {
 };
 size_t group_norm_workspace(const GroupNormProblem& p);  // bytes the launch plan needs (0: none)
 hipError_t launch_group_norm(const GroupNormProblem& p);
+// The allocation-free form's fixed per-device workspace (a static device
+// array of kGnStaticScratchBytes): its device address on the current device.
+constexpr size_t kGnStaticScratchBytes = 256 * 1024;  // 16384 slices of tagged moments
+hipError_t group_norm_static_scratch(void** ptr);
 
 // GELU-gated product: h [rows][2F] -> out [rows][F].
 struct GegluProblem {

@@ -16,6 +16,7 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "attn_internal.h"
@@ -825,7 +826,36 @@ hipError_t launch_geglu_e(const GegluProblem& p) {
   return hipGetLastError();
 }
 
+// Scratch of the allocation-free group normalisation (attn_group_norm_static):
+// one array per device, the workspace of every such call on that device.
+// Zero at load (static storage), which is the state the split forms expect
+// before their first use; they leave it ready for the next call.  Host code
+// must not pass the array's name to a kernel (on the host it only stands for
+// the symbol): its device address comes from hipGetSymbolAddress below.
+__device__ __align__(256) unsigned long long scratch[kGnStaticScratchBytes / 8];
+
 }  // namespace
+
+hipError_t group_norm_static_scratch(void** ptr) {
+  // device address of `scratch`, looked up once per device with that device
+  // current (every device holds its own copy at its own address)
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_group_norm(const GroupNormProblem& p) {
   switch (p.dt) {

@@ -221,6 +221,20 @@ attn_status attn_group_norm(const void* x, const void* gamma, const void* beta, 
                             size_t workspace_bytes, int N, int C, int HW, int G, float eps, attn_dtype dt,
                             void* stream);
 
+/* attn_group_norm for callers that cannot allocate device memory (code
+ * under graph capture, serving loops, harnesses that forbid hipMalloc): the
+ * same computation and kernels, with the workspace taken from a fixed array
+ * of 262144 bytes that the library holds on each device until the process
+ * ends (the first call on a device looks its address up; nothing is
+ * allocated or freed).  Every call on a device shares that device's array,
+ * so calls that overlap in time on one device (different streams, threads
+ * or processes) race and must not be issued.  A problem whose workspace
+ * (attn_group_norm_workspace_size) exceeds 262144 bytes returns
+ * ATTN_ERR_INVALID_ARG before anything is launched; other requirements and
+ * errors as attn_group_norm. */
+attn_status attn_group_norm_static(const void* x, const void* gamma, const void* beta, void* y, int N, int C,
+                                   int HW, int G, float eps, attn_dtype dt, void* stream);
+
 /* Workspace bytes attn_group_norm needs for this problem (0: none), for a
  * call on any stream, captured or not.  The alignment of x and y enters the
  * plan, so pass the pointers that will be used.  Returns 0 for invalid

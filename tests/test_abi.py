@@ -204,6 +204,17 @@ def test_group_norm_and_geglu_validation(lib):
         _lib.ERR_INVALID_ARG
     assert lib.attn_group_norm(P, None, None, P, P, need - 8, 2, 640, 128 * 128, 32, 1e-5, f, None) == \
         _lib.ERR_INVALID_ARG
+    # attn_group_norm_static: the same argument checks, and a problem whose
+    # workspace exceeds the fixed 262144 bytes is refused before launch
+    st = lib.attn_group_norm_static
+    assert st(None, None, None, P, 2, 32, 64, 32, 1e-5, f, None) == _lib.ERR_INVALID_ARG
+    assert st(P, None, None, None, 2, 32, 64, 32, 1e-5, f, None) == _lib.ERR_INVALID_ARG
+    assert st(P, None, None, P, 2, 30, 64, 4, 1e-5, f, None) == _lib.ERR_INVALID_ARG
+    assert st(P, None, None, P, 2, 32, 64, 32, -1.0, f, None) == _lib.ERR_INVALID_ARG
+    assert st(P, None, None, P, 2, 32, 64, 32, 1e-5, 9, None) == _lib.ERR_UNSUPPORTED
+    big = ws(P, P, 1024, 256, 65536, 32, f)
+    assert big > 262144
+    assert st(P, None, None, P, 1024, 256, 65536, 32, 1e-5, f, None) == _lib.ERR_INVALID_ARG
     # attn_geglu(h, out, rows, F, dt, stream)
     ge = lib.attn_geglu
     assert ge(None, P, 4, 8, f, None) == _lib.ERR_INVALID_ARG
