@@ -117,6 +117,17 @@ def block_stats(row, block_lens):
     return m.value, l.value
 
 
+def default_threads() -> int:
+    """Threads of one oracle call: ATTN_ORACLE_THREADS, else OMP_NUM_THREADS,
+    else min(16, cpu count) (rows are independent: the count never changes a
+    result)."""
+    for var in ("ATTN_ORACLE_THREADS", "OMP_NUM_THREADS"):
+        v = os.environ.get(var, "")
+        if v.isdigit() and int(v) > 0:
+            return int(v)
+    return max(1, min(16, os.cpu_count() or 1))
+
+
 def attention(q, k, v, scale: float, nthreads: int | None = None):
     """Attention over [..., N, d] tensors (leading dims are heads).
 
@@ -132,7 +143,7 @@ def attention(q, k, v, scale: float, nthreads: int | None = None):
     o = np.empty(q.shape, np.float64)
     ml = np.empty(lead + (nq, 2), np.float64)
     if nthreads is None:
-        nthreads = os.cpu_count() or 1
+        nthreads = default_threads()
     rc = _load().oracle_attention(_dp(q), _dp(k), _dp(v), bh, nq, nk, d, float(scale),
                                   _dp(o), _dp(ml), int(nthreads))
     if rc != 0:

@@ -14,6 +14,10 @@ TOL = {
     "f32": dict(max=1e-5, mean=1e-6),
 }
 STATS_RTOL = 1e-3
+# m is held to STATS_RTOL relative to |m_ref|, with |m_ref| floored at M_FLOOR:
+# a row whose largest logit is within 0.01 of zero is held to 1e-5 absolute
+# (a relative error of a quantity near zero says nothing about the kernel)
+M_FLOOR = 1e-2
 
 
 def to_device(a: np.ndarray, dtype: str):
@@ -53,7 +57,7 @@ def assert_close_o(o_gpu: np.ndarray, o_ref: np.ndarray, dtype: str, what: str =
 def assert_close_ml(ml_gpu: np.ndarray, ml_ref: np.ndarray, what: str = ""):
     m, l = ml_gpu[..., 0], ml_gpu[..., 1]
     mr, lr = ml_ref[..., 0], ml_ref[..., 1]
-    em = np.abs(m - mr) / np.maximum(1.0, np.abs(mr))
+    em = np.abs(m - mr) / np.maximum(M_FLOOR, np.abs(mr))
     el = np.abs(l - lr) / lr
     assert np.isfinite(ml_gpu).all(), f"{what}: non-finite stats"
     assert em.max() <= STATS_RTOL, f"{what}: m rel err {em.max():.3e}"

@@ -1,7 +1,10 @@
 """GPU parity: every entry point of libattn.so against the float64 oracle on
-the seeded SD UNet attention workloads (full outputs where the oracle is
-cheap, sampled query rows at the two large self-attention sizes), in the
-element types the library supports, plus ragged and degenerate shapes."""
+the seeded SD UNet attention workloads, every output element compared
+(including the two full-size self-attention configs, with sampled-row runs
+kept as fast checks), in the element types the library supports, plus ragged
+and degenerate shapes."""
+import json
+
 import numpy as np
 import pytest
 
@@ -41,6 +44,7 @@ def _run_all(cfg: Config, dtype: str, rows=None):
             assert_close_ml(sel(from_device(ml3)), ml_ref, f"{cfg.name}/{dtype}/forward pf ml")
     torch.cuda.synchronize()
     print(cfg.name, dtype, {k_: tuple(f"{x:.2e}" for x in v_) for k_, v_ in results.items()}, flush=True)
+    return results
 
 
 @pytest.mark.parametrize("name", SMALL)
@@ -59,6 +63,21 @@ def test_small_configs_other_dtypes(name, dtype):
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_tiny_in_half_types(name, dtype):
     _run_all(CONFIGS[name], dtype)
+
+
+@pytest.mark.parametrize("name", LARGE)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_full_size_every_row(name, dtype):
+    # the whole output and (m, l) of every form against the oracle (about 1 s
+    # of oracle time at 4096 x 4096 and 10-15 s at 16384 x 16384 on 16 threads)
+    import time
+    cfg = CONFIGS[name]
+    t0 = time.perf_counter()
+    res = _run_all(cfg, dtype)
+    rec = {"config": name, "dtype": dtype, "seconds": round(time.perf_counter() - t0, 1),
+           "o_max_mean_abs": {k_: v_ for k_, v_ in res.items() if k_ not in ("stats", "flash_ml")},
+           "ml_rel_m_l": {k_: res[k_] for k_ in ("stats", "flash_ml")}}
+    print("PARITY " + json.dumps(rec), flush=True)
 
 
 @pytest.mark.parametrize("name", LARGE)
