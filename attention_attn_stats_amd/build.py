@@ -15,7 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libattn.so")
-SOURCES = ["attn_api.cpp", "attn_mfma.hip", "attn_fa40.hip", "attn_f32.hip", "attn_scores.hip", "unet_ops.hip"]
+SOURCES = ["attn_api.cpp", "attn_mfma.hip", "attn_fa40.hip", "attn_f32.hip", "attn_scores.hip", "unet_ops.hip",
+           "attn_fill.hip"]
 ARCH = os.environ.get("ATTN_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

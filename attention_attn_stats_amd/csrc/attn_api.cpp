@@ -182,6 +182,7 @@ const char* attn_status_string(attn_status s) {
     case ATTN_ERR_INVALID_ARG: return "invalid argument";
     case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension, element type or variant";
     case ATTN_ERR_HIP: return "HIP runtime error";
+    default: break;
   }
   return "unknown status";
 }
@@ -500,8 +501,9 @@ attn_variant attn_select(int B, int H, int Nq, int Nk, int d, attn_dtype dt, voi
   attn_variant chosen = ATTN_AUTO;
   if (hipMalloc(&bq, nq) == hipSuccess && hipMalloc(&bk, nk) == hipSuccess && hipMalloc(&bv, nk) == hipSuccess &&
       hipMalloc(&bo, nq) == hipSuccess && hipMalloc(&bml, (size_t)p.BH * Nq * 2 * sizeof(float)) == hipSuccess &&
-      hipMemsetAsync(bq, 0, nq, p.stream) == hipSuccess && hipMemsetAsync(bk, 0, nk, p.stream) == hipSuccess &&
-      hipMemsetAsync(bv, 0, nk, p.stream) == hipSuccess) {
+      attn::launch_fill_uniform(bq, nq / esz, dt, 1, p.stream) == hipSuccess &&
+      attn::launch_fill_uniform(bk, nk / esz, dt, 2, p.stream) == hipSuccess &&
+      attn::launch_fill_uniform(bv, nk / esz, dt, 3, p.stream) == hipSuccess) {
     p.q = bq;
     p.k = bk;
     p.v = bv;

@@ -62,6 +62,10 @@ hipError_t launch_scores(const Problem& p, float* a);                   // A = s
 hipError_t launch_scores_stats(const float* a, float* ml, long long rows, int Nk, hipStream_t stream);
 hipError_t launch_mfma_pv_scores(const Problem& p);                     // O from p.a, p.ml, p.v
 
+// Seeded stand-in values (uniform, zero mean, unit variance) for n elements
+// of type dt at p: the data the variant selector times a shape on.
+hipError_t launch_fill_uniform(void* p, size_t n, attn_dtype dt, unsigned seed, hipStream_t stream);
+
 // Group normalisation of x [N][C][HW] (y may equal x).  The workspace is
 // needed only by groups too large for one workgroup's registers.
 struct GroupNormProblem {

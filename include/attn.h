@@ -71,15 +71,20 @@ typedef enum {
                                aligned (ml: 8-byte), dimension < 1, scale not
                                finite and > 0, tensor of 2^31 or more elements */
   ATTN_ERR_UNSUPPORTED = 2, /* d not in {40, 80, 160}, unknown dtype/variant */
-  ATTN_ERR_HIP = 3          /* the HIP runtime reported an error */
+  ATTN_ERR_HIP = 3,         /* the HIP runtime reported an error */
+  ATTN_STATUS_INT_ = 0x7fffffff
 } attn_status;
 
-typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 } attn_dtype;
+/* (The *_INT_ members are not values: they give each enumeration the range of
+ * int, so that an out-of-range value passed by a caller is an argument the
+ * library refuses, not undefined behaviour in the C++ implementation.) */
+typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2, ATTN_DTYPE_INT_ = 0x7fffffff } attn_dtype;
 
 typedef enum {
   ATTN_AUTO = 0,          /* pick by measurement, cached per shape */
   ATTN_PARTIAL_FUSED = 1, /* attn_stats then attn_pv */
-  ATTN_FLASH = 2          /* attn_flash */
+  ATTN_FLASH = 2,         /* attn_flash */
+  ATTN_VARIANT_INT_ = 0x7fffffff
 } attn_variant;
 
 /* Partially fused softmax, pass 1: per-row statistics of A = scale * Q K^T.
@@ -252,9 +257,12 @@ size_t attn_group_norm_workspace_size(const void* x, const void* y, int N, int C
 attn_status attn_geglu(const void* h, void* out, int rows, int F, attn_dtype dt, void* stream);
 
 /* The variant ATTN_AUTO uses for this shape.  On a cache miss it allocates
- * temporary device buffers, times both variants on `stream`, frees the
- * buffers and caches the winner, so it synchronises and may allocate; call it
- * outside timed regions.  On a stream being captured into a graph a cache
+ * temporary device buffers, fills q, k and v with seeded stand-in values
+ * (uniform, zero mean, unit variance: non-zero data like the activations it
+ * stands for), times both variants on `stream`, frees the buffers and caches
+ * the winner, so it synchronises and may allocate; call it outside timed
+ * regions.  (attn_forward with ATTN_AUTO times a cache miss on the caller's
+ * own buffers instead.)  On a stream being captured into a graph a cache
  * miss returns attn_default_variant(d) without timing or caching.  Returns
  * ATTN_AUTO (0) on error. */
 attn_variant attn_select(int B, int H, int Nq, int Nk, int d, attn_dtype dt, void* stream);

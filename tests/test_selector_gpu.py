@@ -129,3 +129,26 @@ def test_auto_forward_in_place_over_q(monkeypatch):
         expect = ref if form == "pf" else attn.flash(tq, tk, tv, scale=scale)
         torch.cuda.synchronize()
         assert torch.equal(inplace, expect), form
+
+
+@pytest.mark.parametrize("name", ["sd512_self", "level2_self"])
+def test_select_agrees_with_auto_forward_on_the_workload(name, monkeypatch):
+    # attn_select times a shape on seeded stand-in values; an ATTN_AUTO
+    # forward times it on the caller's own buffers.  On the seeded workload
+    # of a config both must cache the same form.
+    import torch
+    import attention_attn_stats_amd as attn
+    monkeypatch.delenv("ATTN_VARIANT", raising=False)
+    monkeypatch.setenv("ATTN_SELECT_ITERS", "9")
+    cfg = CONFIGS[name]
+    q, k, v = (to_device(x, cfg.dtype) for x in cfg.inputs())
+    tdt = q.dtype
+    attn.select_reset()
+    attn.forward(q, k, v, variant="auto", scale=cfg.scale)
+    torch.cuda.synchronize()
+    from_forward = attn.select(cfg.B, cfg.H, cfg.Nq, cfg.Nk, cfg.d, tdt)  # the cached choice
+    attn.select_reset()
+    from_select = attn.select(cfg.B, cfg.H, cfg.Nq, cfg.Nk, cfg.d, tdt)
+    print(name, "forward:", from_forward, "select:", from_select, flush=True)
+    assert from_forward == from_select
+    attn.select_reset()
