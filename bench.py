@@ -1,10 +1,12 @@
 #!/usr/bin/env python3
 """Throughput of the SD UNet attention hot path on one MI355X.
 
-One step = one full attention forward (attn_forward with the variant the
-per-shape selector picks, i.e. every kernel of the chosen form) over the
-seeded synthetic inputs of the SD 512x512 top-level self-attention
-(B=2, H=8, Nq=Nk=4096, d=40, fp16), inputs already resident in HBM.
+One step = the attention forward over the seeded synthetic inputs of the SD
+512x512 top-level self-attention (B=2, H=8, Nq=Nk=4096, d=40, fp16), inputs
+already resident in HBM, in the form the per-shape selector picks (attn_select,
+as attn_forward with ATTN_AUTO would), issued kernel by kernel as attn_forward
+issues it: attn_flash for the single pass, or attn_stats then attn_pv for the
+partially fused form.  With --variant the form is fixed instead.
 
 Prints ONE JSON line with the headline metric (useful attention TFLOP/s,
 4*B*H*Nq*Nk*d per step, and its fraction of the fp16 dense MFMA peak), the
@@ -33,42 +35,52 @@ if ROOT not in sys.path:
 METRIC = "attention TFLOP/s + % fp16 MFMA peak @ B=2,H=8,N=4096,d=40"
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}  # dense MFMA (fp16/bf16); fp32 vector
 HBM_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "attention_attn_stats_amd", "csrc", "attn_mfma.hip")
+CSRC = os.path.join(ROOT, "attention_attn_stats_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source(kernel: str, cfg) -> str:
+    """Source file of the kernel a launch runs: the head-dim-40 kernels
+    (attn_fa40.hip) for the single pass and the second pass at d = 40 in the
+    half types (unless ATTN_FA40=0 selects the general kernel), else the
+    general matrix-core kernels (attn_mfma.hip)."""
+    fa40 = (cfg.d == 40 and cfg.dtype in ("f16", "bf16") and kernel in ("attn_flash", "attn_pv")
+            and os.environ.get("ATTN_FA40", "1")[:1] != "0")
+    return os.path.join(CSRC, "attn_fa40.hip" if fa40 else "attn_mfma.hip")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_hash() -> str:
-    """Hash of the kernel source without its comments and blank space, and
-    of the compile flags of that file alone, so that a comment edit does not
+def kernel_hash(path: str) -> str:
+    """Hash of a kernel source without its comments and blank space, and of
+    the compile flags of that file alone, so that a comment edit does not
     orphan counters taken on the same code but a flag that changes the code
     does."""
     import re
     from attention_attn_stats_amd import build as _build
-    with open(KERNEL_SRC) as f:
+    with open(path) as f:
         src = f.read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     src = re.sub(r"//[^\n]*", "", src)
     src = "\n".join(ln.strip() for ln in src.splitlines() if ln.strip())
-    flags = _build.FILE_FLAGS.get(os.path.basename(KERNEL_SRC), [])
+    flags = _build.FILE_FLAGS.get(os.path.basename(path), [])
     if flags:
         src += "\n#flags " + " ".join(flags)
     return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
-def load_traffic(kernel: str, workload: str):
+def load_traffic(kernel: str, cfg):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary, if it was taken on the current kernel source; else None."""
+    summary, if it was taken on the current source of the kernel; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    e = t.get(f"{kernel}@{workload}")
-    if not e or e.get("kernel_src_sha256_16") != kernel_hash():
+    e = t.get(f"{kernel}@{cfg.name}")
+    if not e or e.get("kernel_src_sha256_16") != kernel_hash(kernel_source(kernel, cfg)):
         return None
     return e.get("bytes_per_launch")
 
@@ -356,6 +368,18 @@ def oracle_single_thread(cfg) -> dict:
 SMALL_FOR_ORACLE = ("tiny", "tiny8", "sd512_cross", "level2_self", "level3_self", "level4_self")
 
 
+def oracle_threads_whole(cfg) -> dict:
+    """The float64 oracle over the whole config on the default thread count
+    (what a full-output parity check of the config costs)."""
+    import oracle
+    from attention_attn_stats_amd import synth
+    threads = oracle.default_threads()
+    q, k, v = (synth.widen(x, cfg.dtype) for x in cfg.inputs())
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, cfg.scale, nthreads=threads)
+    return {"oracle_threads": threads, "oracle_threads_s": round(time.perf_counter() - t0, 3)}
+
+
 def oracle_single_thread_sampled(cfg, rows: int = 256) -> dict:
     """The float64 oracle on one host thread over the first `rows` query rows
     of the first head (against all Nk keys), and the whole config's time
@@ -373,15 +397,38 @@ def oracle_single_thread_sampled(cfg, rows: int = 256) -> dict:
             "oracle_1thread_extrapolated_from": f"{rows} query rows of one head ({t:.4f} s)"}
 
 
-def cpu_model() -> str:
+def host_cpu() -> dict:
+    """The host CPU as /proc/cpuinfo describes it: the model name, family /
+    model / stepping, logical CPUs and physical cores (distinct (package,
+    core) pairs), and the logical CPUs this process may run on."""
+    info = {"model_name": "unknown"}
+    pairs, logical, fields = set(), 0, {}
     try:
         with open("/proc/cpuinfo") as f:
             for ln in f:
-                if ln.startswith("model name"):
-                    return ln.split(":", 1)[1].strip()
+                if ":" not in ln:
+                    if "core id" in fields:
+                        pairs.add((fields.get("physical id", "0"), fields["core id"]))
+                    fields = {}
+                    continue
+                k_, v_ = (x.strip() for x in ln.split(":", 1))
+                fields[k_] = v_
+                if k_ == "processor":
+                    logical += 1
+                elif k_ in ("model name", "cpu family", "model", "stepping", "vendor_id") and \
+                        k_.replace(" ", "_") not in info or (k_ == "model name" and info["model_name"] == "unknown"):
+                    info[k_.replace(" ", "_")] = v_
+        if "core id" in fields:
+            pairs.add((fields.get("physical id", "0"), fields["core id"]))
     except OSError:
         pass
-    return "unknown"
+    info["logical_cpus"] = logical or (os.cpu_count() or 0)
+    info["physical_cores"] = len(pairs) or None
+    try:
+        info["cpus_available_to_process"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        info["cpus_available_to_process"] = os.cpu_count()
+    return info
 
 
 def cpu_baseline(cfg, budget_s: float = 20.0):
@@ -390,7 +437,7 @@ def cpu_baseline(cfg, budget_s: float = 20.0):
     heads as fill about `budget_s` seconds of wall time."""
     import oracle
     from attention_attn_stats_amd import synth
-    threads = min(16, os.cpu_count() or 1)
+    threads = oracle.default_threads()
     bh = cfg.B * cfg.H
     q, k, v = (synth.widen(x, cfg.dtype).reshape(bh, -1, cfg.d) for x in cfg.inputs())
     t0 = time.perf_counter()
@@ -406,7 +453,7 @@ def cpu_baseline(cfg, budget_s: float = 20.0):
     t = time.perf_counter() - t0
     flops = 4.0 * done * cfg.Nq * cfg.Nk * cfg.d
     return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "cpu": cpu_model(),
+            "threads_used": threads, "host": host_cpu(),
             "sample": f"{done} head evaluations ({done / bh:.1f} passes over the {bh} heads of {cfg.name}; "
                       f"each {cfg.Nq} queries x {cfg.Nk} keys x d={cfg.d}, float64, score matrix "
                       f"materialised), {t:.1f} s wall"}
@@ -464,8 +511,9 @@ def main():
     achieved = kflops / (kms * 1e-3) / 1e12
     kernel_id = {"flash": "attn_flash", "stats": "attn_stats", "pv": "attn_pv"}[kname]
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4), "traffic": load_traffic(kernel_id, cfg.name),
-            "kernel": kernel_id, "kernel_ms": round(kms, 5)}
+            "frac": round(achieved / peak, 4), "traffic": load_traffic(kernel_id, cfg),
+            "kernel": kernel_id, "kernel_src": os.path.basename(kernel_source(kernel_id, cfg)),
+            "kernel_ms": round(kms, 5)}
     line = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5),
@@ -482,10 +530,13 @@ def main():
     }
     if args.configs_out:
         with open(args.configs_out, "w") as f:
+            import attention_attn_stats_amd as attn
+            tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
             for name, c in CONFIGS.items():
-                cpu = {}
+                cpu = {"auto_choice": attn.select(c.B, c.H, c.Nq, c.Nk, c.d, tdt[c.dtype])}
                 if not args.no_cpu_baseline:
-                    cpu = oracle_single_thread(c) if name in SMALL_FOR_ORACLE else oracle_single_thread_sampled(c)
+                    cpu.update(oracle_single_thread(c) if name in SMALL_FOR_ORACLE else oracle_single_thread_sampled(c))
+                    cpu.update(oracle_threads_whole(c))
                 for var in args.forms.split(","):
                     if var == "pf_scores" and c.dtype == "f32":
                         continue  # the stored-logit path runs on the matrix cores only

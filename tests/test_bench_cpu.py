@@ -50,23 +50,37 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_traffic_is_reported_only_for_the_profiled_source(tmp_path, monkeypatch):
+    from attention_attn_stats_amd.configs import CONFIGS
+    cfg = CONFIGS["sd512_self"]
     src = tmp_path / "kernel.hip"
     src.write_text("int f() {\n  return 1;  // one\n}\n/* block */\n")
-    monkeypatch.setattr(bench, "KERNEL_SRC", str(src))
-    h = bench.kernel_hash()
+    monkeypatch.setattr(bench, "kernel_source", lambda kernel, c: str(src))
+    h = bench.kernel_hash(str(src))
     tf = tmp_path / "traffic.json"
     tf.write_text(json.dumps({"attn_flash@sd512_self": {"kernel_src_sha256_16": h, "bytes_per_launch": 123}}))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tf))
-    assert bench.load_traffic("attn_flash", "sd512_self") == 123
+    assert bench.load_traffic("attn_flash", cfg) == 123
     # comments and blank space do not count ...
     src.write_text("int f() {\n\n    return 1;  // changed comment\n}\n/* other */\n")
-    assert bench.kernel_hash() == h and bench.load_traffic("attn_flash", "sd512_self") == 123
+    assert bench.kernel_hash(str(src)) == h and bench.load_traffic("attn_flash", cfg) == 123
     # ... code does
     src.write_text("int f() {\n  return 2;\n}\n")
-    assert bench.kernel_hash() != h and bench.load_traffic("attn_flash", "sd512_self") is None
-    assert bench.load_traffic("attn_flash", "other_workload") is None
+    assert bench.kernel_hash(str(src)) != h and bench.load_traffic("attn_flash", cfg) is None
+    assert bench.load_traffic("attn_flash", CONFIGS["sd1024_self"]) is None
     # ... and so do compile flags given to that file alone
     from attention_attn_stats_amd import build
-    h2 = bench.kernel_hash()
+    h2 = bench.kernel_hash(str(src))
     monkeypatch.setitem(build.FILE_FLAGS, "kernel.hip", ["-mllvm", "-some-option"])
-    assert bench.kernel_hash() != h2
+    assert bench.kernel_hash(str(src)) != h2
+
+
+def test_kernel_source_follows_the_dispatch(monkeypatch):
+    from attention_attn_stats_amd.configs import CONFIGS
+    monkeypatch.delenv("ATTN_FA40", raising=False)
+    c1 = CONFIGS["sd512_self"]
+    assert bench.kernel_source("attn_flash", c1).endswith("attn_fa40.hip")
+    assert bench.kernel_source("attn_pv", c1).endswith("attn_fa40.hip")
+    assert bench.kernel_source("attn_stats", c1).endswith("attn_mfma.hip")
+    assert bench.kernel_source("attn_flash", CONFIGS["level3_self"]).endswith("attn_mfma.hip")  # d = 160
+    monkeypatch.setenv("ATTN_FA40", "0")
+    assert bench.kernel_source("attn_flash", c1).endswith("attn_mfma.hip")
