@@ -589,27 +589,31 @@ hipError_t by_type(const Problem& p) {
   return p.dt == ATTN_BF16 ? by_dim<L, BF16>(p) : by_dim<L, F16>(p);
 }
 
-// Whether head dimension 40 takes the software-pipelined kernel of
-// attn_fa40.hip (the default) or this file's (ATTN_FA40=0, for comparison).
-bool use_fa40() {
-  static const bool on = [] {
-    const char* e = std::getenv("ATTN_FA40");
-    return !(e && e[0] == '0');
-  }();
-  return on;
+// Whether a head-dimension-40 problem takes the kernel of attn_fa40.hip or
+// this file's.  Measured on MI355X (both kernels, graph-replayed launches, B=2,
+// H=8): the attn_fa40.hip kernel is 3-4 % faster where all its workgroups are
+// resident at once (one 256-query workgroup per CU) and the key range is long
+// (Nq = 4096 with 4096-8192 keys), level with this file's from 2048 keys, and
+// 5-17 % slower with fewer keys or when its workgroups run in several rounds
+// (Nq = 16384: 1024 workgroups); so it takes exactly the former.  ATTN_FA40=0
+// turns it off, ATTN_FA40=1 forces it wherever d = 40 (for comparisons).
+bool use_fa40(const Problem& p, int cus) {
+  const char* e = std::getenv("ATTN_FA40");  // (read per launch: tests switch it)
+  if (e && (e[0] == '0' || e[0] == '1')) return e[0] == '1';
+  return (long long)p.BH * ((p.Nq + 255) / 256) <= cus && p.Nk >= 2048;
 }
 
 template <class TR, int D> struct StatsL { static hipError_t run(const Problem& p) { return launch_fwd_t<TR, D, kModeStats>(p); } };
 template <class TR, int D> struct PvL {
   static hipError_t run(const Problem& p) {
-    if (D == 40 && use_fa40()) return launch_fa40_pv(p, cu_count());
+    if (D == 40 && use_fa40(p, cu_count())) return launch_fa40_pv(p, cu_count());
     return launch_fwd_t<TR, D, kModePV>(p);
   }
 };
 template <class TR, int D> struct PvAL { static hipError_t run(const Problem& p) { return launch_fwd_t<TR, D, kModePVScores>(p); } };
 template <class TR, int D> struct FlashL {
   static hipError_t run(const Problem& p) {
-    if (D == 40 && use_fa40()) return launch_fa40_flash(p, cu_count());
+    if (D == 40 && use_fa40(p, cu_count())) return launch_fa40_flash(p, cu_count());
     return p.ml ? launch_fwd_t<TR, D, kModeFlashML>(p) : launch_fwd_t<TR, D, kModeFlash>(p);
   }
 };

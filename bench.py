@@ -39,13 +39,16 @@ CSRC = os.path.join(ROOT, "attention_attn_stats_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_source(kernel: str, cfg) -> str:
-    """Source file of the kernel a launch runs: the head-dim-40 kernels
-    (attn_fa40.hip) for the single pass and the second pass at d = 40 in the
-    half types (unless ATTN_FA40=0 selects the general kernel), else the
-    general matrix-core kernels (attn_mfma.hip)."""
-    fa40 = (cfg.d == 40 and cfg.dtype in ("f16", "bf16") and kernel in ("attn_flash", "attn_pv")
-            and os.environ.get("ATTN_FA40", "1")[:1] != "0")
+def kernel_source(kernel: str, cfg, cus: int = 256) -> str:
+    """Source file of the kernel a launch runs, by the library's dispatch rule:
+    the head-dim-40 kernels of attn_fa40.hip for the single pass and the second
+    pass at d = 40 in the half types when every 256-query workgroup is resident
+    at once (B*H*ceil(Nq/256) <= the CU count) and Nk >= 2048 (ATTN_FA40=0 / 1
+    turn that off / force it), else the general kernels of attn_mfma.hip."""
+    env = os.environ.get("ATTN_FA40", "")[:1]
+    rule = cfg.B * cfg.H * -(-cfg.Nq // 256) <= cus and cfg.Nk >= 2048
+    on = {"0": False, "1": True}.get(env, rule)
+    fa40 = cfg.d == 40 and cfg.dtype in ("f16", "bf16") and kernel in ("attn_flash", "attn_pv") and on
     return os.path.join(CSRC, "attn_fa40.hip" if fa40 else "attn_mfma.hip")
 
 
@@ -473,6 +476,10 @@ def main():
     ap.add_argument("--cold", action="store_true")
     ap.add_argument("--unet-ops-out", default=None,
                     help="also time group_norm and geglu at the UNet's sizes, JSONL there")
+    ap.add_argument("--sweep-keys", default=None, metavar="NK,NK,...",
+                    help="only time the chosen form of --config at each of these key counts "
+                         "(seeded inputs, 50 launches each, one JSON line per count) and exit: "
+                         "the fixed cost of a dispatch is the intercept")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times (calibrates the "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -493,11 +500,20 @@ def main():
         sys.exit(2)
 
     import torch
-    from attention_attn_stats_amd.configs import CONFIGS
+    from attention_attn_stats_amd.configs import CONFIGS, Config
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     cfg = CONFIGS[args.config]
+    if args.sweep_keys:
+        for nk in (int(x) for x in args.sweep_keys.split(",")):
+            c = Config(f"{cfg.name}_nk{nk}", cfg.index, cfg.B, cfg.H, cfg.Nq, nk, cfg.d, cfg.dtype, cfg.sigma_qk,
+                       cfg.sigma_v)
+            t = time_steps(c, "flash" if args.variant != "pf" else "pf", 50, 5, False)
+            print(json.dumps({"config": cfg.name, "Nk": nk, "form": "flash" if args.variant != "pf" else "pf",
+                              "median_us": round(t["median_ms"] * 1e3, 2),
+                              "graph_us": round(t.get("graph_ms", float("nan")) * 1e3, 2)}), flush=True)
+        return
     r = time_config(cfg, args.variant, args.steps, args.warmup)
     flops = cfg.flops
     tflops = flops / (r["ms_per_step"] * 1e-3) / 1e12

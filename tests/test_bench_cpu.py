@@ -82,5 +82,9 @@ def test_kernel_source_follows_the_dispatch(monkeypatch):
     assert bench.kernel_source("attn_pv", c1).endswith("attn_fa40.hip")
     assert bench.kernel_source("attn_stats", c1).endswith("attn_mfma.hip")
     assert bench.kernel_source("attn_flash", CONFIGS["level3_self"]).endswith("attn_mfma.hip")  # d = 160
+    assert bench.kernel_source("attn_flash", CONFIGS["sd1024_self"]).endswith("attn_mfma.hip")  # 1024 workgroups
+    assert bench.kernel_source("attn_flash", CONFIGS["sd512_cross"]).endswith("attn_mfma.hip")  # 77 keys
+    monkeypatch.setenv("ATTN_FA40", "1")
+    assert bench.kernel_source("attn_flash", CONFIGS["sd1024_self"]).endswith("attn_fa40.hip")
     monkeypatch.setenv("ATTN_FA40", "0")
     assert bench.kernel_source("attn_flash", c1).endswith("attn_mfma.hip")

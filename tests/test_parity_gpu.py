@@ -113,3 +113,20 @@ def test_ragged_shapes(shape, dtype):
     B, H, Nq, Nk, d = shape
     cfg = Config(f"ragged_{'x'.join(map(str, shape))}", 50 + sum(shape), B, H, Nq, Nk, d, dtype)
     _run_all(cfg, dtype)
+
+
+# The head-dimension-40 kernel of attn_fa40.hip runs by default only where it
+# is the faster one (every workgroup resident, long key ranges); forced here
+# onto ragged and degenerate shapes (partial key blocks, one key, partial
+# query tiles, more than one round of workgroups).
+FA40_FORCED = [(1, 1, 1, 1), (1, 2, 5, 3), (2, 3, 77, 77), (1, 2, 200, 65), (1, 1, 129, 63),
+               (1, 2, 300, 2049), (2, 8, 1000, 130), (1, 1, 4096, 64)]
+
+
+@pytest.mark.parametrize("shape", FA40_FORCED, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_fa40_kernel_forced_on_ragged_shapes(shape, dtype, monkeypatch):
+    monkeypatch.setenv("ATTN_FA40", "1")
+    B, H, Nq, Nk = shape
+    cfg = Config(f"fa40_{'x'.join(map(str, shape))}", 70 + sum(shape), B, H, Nq, Nk, 40, dtype)
+    _run_all(cfg, dtype)
