@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libattn.so")
 SOURCES = ["attn_api.cpp", "attn_mfma.hip", "attn_fa40.hip", "attn_f32.hip", "attn_scores.hip", "unet_ops.hip",
-           "attn_fill.hip"]
+           "attn_fill.hip", "attn_short.hip"]
 ARCH = os.environ.get("ATTN_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
@@ -69,7 +69,7 @@ def unverified_mfma(asm_text: str) -> list:
     return bad
 
 
-MFMA_SOURCES = ["attn_mfma.hip", "attn_fa40.hip", "attn_scores.hip"]
+MFMA_SOURCES = ["attn_mfma.hip", "attn_fa40.hip", "attn_scores.hip", "attn_short.hip"]
 
 
 def verify_device_code(hipcc: str, verbose: bool = False, defines=()) -> None:

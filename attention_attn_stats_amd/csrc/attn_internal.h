@@ -56,6 +56,10 @@ hipError_t launch_mfma_flash(const Problem& p);  // writes p.ml when it is non-n
 // strided); `cus` = compute units of the device.
 hipError_t launch_fa40_flash(const Problem& p, int cus);  // writes p.ml when it is non-null
 hipError_t launch_fa40_pv(const Problem& p, int cus);
+// The short-key-range single pass (attn_short.hip): every key of a head in
+// one block per wave, for Nk <= short_max_keys(d) (0 for unsupported d).
+int short_max_keys(int d);
+hipError_t launch_short_flash(const Problem& p, int cus);  // writes p.ml when it is non-null
 
 // The partially fused form over a stored logit matrix A (float32).
 hipError_t launch_scores(const Problem& p, float* a);                   // A = scale Q K^T

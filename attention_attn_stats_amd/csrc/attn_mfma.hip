@@ -603,6 +603,17 @@ bool use_fa40(const Problem& p, int cus) {
   return (long long)p.BH * ((p.Nq + 255) / 256) <= cus && p.Nk >= 2048;
 }
 
+// Whether a single pass takes the short-key-range kernel of attn_short.hip:
+// every key range it supports (with at most 65535 heads and batches: its
+// grid's y and z dimensions).  ATTN_SHORT=0 turns it off, ATTN_SHORT=1 forces it wherever it
+// supports the shape (for comparisons).
+bool use_short(const Problem& p) {
+  if (p.Nk > short_max_keys(p.d) || p.lay.H > 65535 || p.BH / p.lay.H > 65535) return false;
+  const char* e = std::getenv("ATTN_SHORT");  // (read per launch: tests switch it)
+  if (e && (e[0] == '0' || e[0] == '1')) return e[0] == '1';
+  return true;
+}
+
 template <class TR, int D> struct StatsL { static hipError_t run(const Problem& p) { return launch_fwd_t<TR, D, kModeStats>(p); } };
 template <class TR, int D> struct PvL {
   static hipError_t run(const Problem& p) {
@@ -613,6 +624,7 @@ template <class TR, int D> struct PvL {
 template <class TR, int D> struct PvAL { static hipError_t run(const Problem& p) { return launch_fwd_t<TR, D, kModePVScores>(p); } };
 template <class TR, int D> struct FlashL {
   static hipError_t run(const Problem& p) {
+    if (use_short(p)) return launch_short_flash(p, cu_count());
     if (D == 40 && use_fa40(p, cu_count())) return launch_fa40_flash(p, cu_count());
     return p.ml ? launch_fwd_t<TR, D, kModeFlashML>(p) : launch_fwd_t<TR, D, kModeFlash>(p);
   }

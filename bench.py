@@ -41,14 +41,22 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 def kernel_source(kernel: str, cfg, cus: int = 256) -> str:
     """Source file of the kernel a launch runs, by the library's dispatch rule:
-    the head-dim-40 kernels of attn_fa40.hip for the single pass and the second
-    pass at d = 40 in the half types when every 256-query workgroup is resident
-    at once (B*H*ceil(Nq/256) <= the CU count) and Nk >= 2048 (ATTN_FA40=0 / 1
-    turn that off / force it), else the general kernels of attn_mfma.hip."""
+    in the half types, the single pass takes the short-key-range kernel of
+    attn_short.hip where Nk <= 384 (d = 40) or 256 (d = 80, 160) (ATTN_SHORT=0
+    / 1 turn that off / force it within those limits); otherwise the single
+    pass and the second pass at d = 40 take the kernels of attn_fa40.hip when
+    every 256-query workgroup is resident at once (B*H*ceil(Nq/256) <= the CU
+    count) and Nk >= 2048 (ATTN_FA40=0 / 1 turn that off / force it); the
+    general kernels of attn_mfma.hip take the rest."""
+    half = cfg.dtype in ("f16", "bf16")
+    short_max = {40: 384, 80: 256, 160: 256}.get(cfg.d, 0)
+    env_s = os.environ.get("ATTN_SHORT", "")[:1]
+    if half and kernel == "attn_flash" and cfg.Nk <= short_max and env_s != "0":
+        return os.path.join(CSRC, "attn_short.hip")
     env = os.environ.get("ATTN_FA40", "")[:1]
     rule = cfg.B * cfg.H * -(-cfg.Nq // 256) <= cus and cfg.Nk >= 2048
     on = {"0": False, "1": True}.get(env, rule)
-    fa40 = cfg.d == 40 and cfg.dtype in ("f16", "bf16") and kernel in ("attn_flash", "attn_pv") and on
+    fa40 = cfg.d == 40 and half and kernel in ("attn_flash", "attn_pv") and on
     return os.path.join(CSRC, "attn_fa40.hip" if fa40 else "attn_mfma.hip")
 
 

@@ -77,14 +77,22 @@ def test_traffic_is_reported_only_for_the_profiled_source(tmp_path, monkeypatch)
 def test_kernel_source_follows_the_dispatch(monkeypatch):
     from attention_attn_stats_amd.configs import CONFIGS
     monkeypatch.delenv("ATTN_FA40", raising=False)
+    monkeypatch.delenv("ATTN_SHORT", raising=False)
     c1 = CONFIGS["sd512_self"]
     assert bench.kernel_source("attn_flash", c1).endswith("attn_fa40.hip")
     assert bench.kernel_source("attn_pv", c1).endswith("attn_fa40.hip")
     assert bench.kernel_source("attn_stats", c1).endswith("attn_mfma.hip")
-    assert bench.kernel_source("attn_flash", CONFIGS["level3_self"]).endswith("attn_mfma.hip")  # d = 160
+    assert bench.kernel_source("attn_flash", CONFIGS["level2_self"]).endswith("attn_mfma.hip")  # 1024 keys
     assert bench.kernel_source("attn_flash", CONFIGS["sd1024_self"]).endswith("attn_mfma.hip")  # 1024 workgroups
-    assert bench.kernel_source("attn_flash", CONFIGS["sd512_cross"]).endswith("attn_mfma.hip")  # 77 keys
+    for name in ("sd512_cross", "level3_self", "level4_self"):  # 77, 256, 64 keys
+        assert bench.kernel_source("attn_flash", CONFIGS[name]).endswith("attn_short.hip")
+        assert bench.kernel_source("attn_pv", CONFIGS[name]).endswith("attn_mfma.hip")
+    assert bench.kernel_source("attn_flash", CONFIGS["tiny"]).endswith("attn_mfma.hip")  # f32: not the MFMA kernels
     monkeypatch.setenv("ATTN_FA40", "1")
     assert bench.kernel_source("attn_flash", CONFIGS["sd1024_self"]).endswith("attn_fa40.hip")
+    assert bench.kernel_source("attn_flash", CONFIGS["sd512_cross"]).endswith("attn_short.hip")
+    monkeypatch.setenv("ATTN_SHORT", "0")
+    assert bench.kernel_source("attn_flash", CONFIGS["sd512_cross"]).endswith("attn_fa40.hip")
     monkeypatch.setenv("ATTN_FA40", "0")
     assert bench.kernel_source("attn_flash", c1).endswith("attn_mfma.hip")
+    assert bench.kernel_source("attn_flash", CONFIGS["level4_self"]).endswith("attn_mfma.hip")
