@@ -412,7 +412,8 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
 
   run(false);
   // the row sum is row 40 of O^T: register 4 of the second tile on lanes 0-31
-  float lrow = __shfl(o1[4], l32);
+  // (the loop above may end on either of two branches: mfma_settled)
+  float lrow = __shfl(mfma_settled(o1[4]), l32);
   if constexpr (!kPV) {
     // a row whose sum left the fast path's range is recomputed by all waves
     if (nb > 0 && __any(!(lrow < kSumLimit))) redo_flag = 1;
@@ -421,7 +422,7 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
     if (redo_flag) {
       barrier();
       run(true);
-      lrow = __shfl(o1[4], l32);
+      lrow = __shfl(mfma_settled(o1[4]), l32);
     }
   }
   if (nb == 0) {

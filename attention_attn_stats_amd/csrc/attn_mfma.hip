@@ -605,13 +605,12 @@ bool use_fa40(const Problem& p, int cus) {
 
 // Whether a single pass takes the short-key-range kernel of attn_short.hip:
 // every key range it supports (with at most 65535 heads and batches: its
-// grid's y and z dimensions).  ATTN_SHORT=0 turns it off, ATTN_SHORT=1 forces it wherever it
-// supports the shape (for comparisons).
+// grid's y and z dimensions).  ATTN_SHORT=0 turns it off (for comparisons;
+// =s / =w select its shared / per-wave form where the shape allows).
 bool use_short(const Problem& p) {
   if (p.Nk > short_max_keys(p.d) || p.lay.H > 65535 || p.BH / p.lay.H > 65535) return false;
   const char* e = std::getenv("ATTN_SHORT");  // (read per launch: tests switch it)
-  if (e && (e[0] == '0' || e[0] == '1')) return e[0] == '1';
-  return true;
+  return !(e && e[0] == '0');
 }
 
 template <class TR, int D> struct StatsL { static hipError_t run(const Problem& p) { return launch_fwd_t<TR, D, kModeStats>(p); } };

@@ -33,6 +33,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstdlib>
+
 #include "attn_internal.h"
 #include "mfma_common.h"
 
@@ -159,6 +161,11 @@ __global__ __launch_bounds__(256) void short_kernel(const uint16_t* __restrict__
     for (int col = 0; col < CPL; ++col) stg[b][col] = load16(vr, off + 16 * LPR * col);
   }
 
+  // No load is issued once the products have started: a load landing in a
+  // register that an in-flight MFMA has yet to read as its accumulator input
+  // corrupts single lanes (seen on MI355X as single wrong query rows).
+  __builtin_amdgcn_sched_barrier(0);
+
   // ---- scores, tile t: keys kb + 16 t + 4G + i (i = 0..3), query q0 + li
   f4v sc[TPW];
 #pragma unroll
@@ -167,13 +174,13 @@ __global__ __launch_bounds__(256) void short_kernel(const uint16_t* __restrict__
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) sc[t] = TR::mma16(kf[t][ks], qf[ks], sc[t]);
   }
-  if (kb + 16 * TPW > Nk) {
+  // keys past Nk: -inf, by selects without a branch (a branch between the
+  // products and these first reads of their results lets the compiler count
+  // too few wait states on one of the paths)
 #pragma unroll
-    for (int t = 0; t < TPW; ++t)
+  for (int t = 0; t < TPW; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (kb + 16 * t + 4 * G + i >= Nk) sc[t][i] = -INFINITY;
-  }
+    for (int i = 0; i < 4; ++i) sc[t][i] = kb + 16 * t + 4 * G + i < Nk ? sc[t][i] : -INFINITY;
   // exact max of the block (scale > 0: the max of the raw scores), in exp2
   // units; a split past every key keeps -inf and weighs nothing in the merge
   float mx = -INFINITY;
@@ -219,17 +226,23 @@ __global__ __launch_bounds__(256) void short_kernel(const uint16_t* __restrict__
   f4v o[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) o[mt] = (f4v){0.f, 0.f, 0.f, 0.f};
+  // (every V operand read before the first product: no load among them)
   const uint16_t* const va = vs + (4 * G + (li >> 2)) * PV + 4 * (li & 3);
+  s8v vop[(TPW + 1) / 2][MT];
 #pragma unroll
-  for (int j = 0; j < (TPW + 1) / 2; ++j) {
-    const s8v pb = __builtin_bit_cast(s8v, (uint4){pp[2 * j][0], pp[2 * j][1], pp[2 * j + 1][0], pp[2 * j + 1][1]});
+  for (int j = 0; j < (TPW + 1) / 2; ++j)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const s4v v0 = lds_read_tr16(va + 32 * j * PV + 16 * mt);
       const s4v v1 = lds_read_tr16(va + (32 * j + 16) * PV + 16 * mt);
-      const s8v vop = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      o[mt] = TR::mma16(vop, pb, o[mt]);
+      vop[j][mt] = (s8v){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
     }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < (TPW + 1) / 2; ++j) {
+    const s8v pb = __builtin_bit_cast(s8v, (uint4){pp[2 * j][0], pp[2 * j][1], pp[2 * j + 1][0], pp[2 * j + 1][1]});
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) o[mt] = TR::mma16(vop[j][mt], pb, o[mt]);
   }
 
   // ---- row sums: the normaliser and the reported l
@@ -312,6 +325,194 @@ __global__ __launch_bounds__(256) void short_kernel(const uint16_t* __restrict__
   if (split == 0) store_ml(M, Lr);
 }
 
+// Shared form, for many queries per head over at most 96 keys (the text
+// cross-attention): the workgroup's SW waves (16 queries each, all keys)
+// stage K and V once in LDS and share them; a wave that loaded its own
+// copies would send the same bytes through the CU's load path once per 16
+// queries.  Grid: x = block of 16 SW queries, y = head in batch, z = batch.
+constexpr int kSharedW = 8;                 // waves per workgroup
+constexpr int kSharedTiles = 6;             // most 16-key tiles (96 keys)
+template <int D>
+constexpr int shared_pk() { return D == 40 ? 40 : D + 8; }  // K row pitch: 16 rows per ds_read_b128 in distinct banks
+
+template <class TR, int D, int TPW, bool kML>
+__global__ __launch_bounds__(64 * kSharedW) void short_shared_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ out, float* __restrict__ ml, const Layout lay, int Nq, int Nk, float scale) {
+  using S = ShortShape<D>;
+  constexpr int KS = S::KS, MT = S::MT, PV = S::PV, VCH = S::VCH, PK = shared_pk<D>();
+  constexpr int W = kSharedW, T = 64 * W;
+  constexpr int KROWS = 16 * TPW, VROWS = S::vrows(TPW);
+  constexpr bool kValuSum = !S::kOnes || (kML && !TR::kRoundedSumOk);
+  constexpr int kNone = 0x7FFFFFF0;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[KROWS * PK + VROWS * PV];
+  uint16_t* const ks_ = smem;
+  uint16_t* const vs_ = smem + KROWS * PK;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = lane >> 4, li = lane & 15;
+  const int head = blockIdx.z * lay.H + blockIdx.y;
+  const long long qh = blockIdx.z * lay.q.batch + blockIdx.y * lay.q.head, kh = blockIdx.z * lay.k.batch + blockIdx.y * lay.k.head;
+  const long long vh = blockIdx.z * lay.v.batch + blockIdx.y * lay.v.head, oh = blockIdx.z * lay.o.batch + blockIdx.y * lay.o.head;
+  const int q0 = ((int)blockIdx.x * W + wave) * 16;
+  const float c = scale * kLog2e;
+  const int qrs = lay.q.row, krs = lay.k.row, vrs = lay.v.row;
+  const bool padlane = S::kPadQK && 32 * (KS - 1) + 8 * G >= D;
+
+  // ---- every load at once: this wave's Q; the workgroup's K and V rows
+  // (16-byte chunk idx = tid + T j: row idx / VCH, chunk idx % VCH); keys
+  // past Nk read as zero
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(q + qh, ((unsigned)(Nq - 1) * (unsigned)qrs + D) * 2u);
+  const unsigned qoff = ((unsigned)(q0 + li) * (unsigned)qrs + 8 * G) * 2u;
+  s8v qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    qf[ks] = __builtin_bit_cast(s8v, load16(qr, (ks == KS - 1 && padlane) ? kNone : (int)(qoff + 64 * ks)));
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + kh, ((unsigned)(Nk - 1) * (unsigned)krs + D) * 2u);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + vh, ((unsigned)(Nk - 1) * (unsigned)vrs + D) * 2u);
+  constexpr int KJ = (KROWS * VCH + T - 1) / T, VJ = (VROWS * VCH + T - 1) / T;
+  uint4 kst[KJ], vst[VJ];
+#pragma unroll
+  for (int j = 0; j < KJ; ++j) {
+    const int idx = tid + T * j, r = idx / VCH, col = idx - r * VCH;
+    kst[j] = load16(kr, idx < KROWS * VCH ? (int)(((unsigned)r * (unsigned)krs + 8 * col) * 2u) : kNone);
+  }
+#pragma unroll
+  for (int j = 0; j < VJ; ++j) {
+    const int idx = tid + T * j, r = idx / VCH, col = idx - r * VCH;
+    // rows past the tiles (to the end of the last 32-key step) as zeros
+    vst[j] = load16(vr, r < KROWS ? (int)(((unsigned)r * (unsigned)vrs + 8 * col) * 2u) : kNone);
+  }
+#pragma unroll
+  for (int j = 0; j < KJ; ++j) {
+    const int idx = tid + T * j, r = idx / VCH, col = idx - r * VCH;
+    if (idx < KROWS * VCH) *(uint4*)(ks_ + r * PK + 8 * col) = kst[j];
+  }
+#pragma unroll
+  for (int j = 0; j < VJ; ++j) {
+    const int idx = tid + T * j, r = idx / VCH, col = idx - r * VCH;
+    if (idx < VROWS * VCH) *(uint4*)(vs_ + r * PV + 8 * col) = vst[j];
+  }
+  if constexpr (S::kOnes) {
+    // V columns D .. PV-1: 1.0 in column D (the row-sum dim), zeros after it
+    for (int r = tid; r < VROWS; r += T) *(uint4*)(vs_ + r * PV + D) = make_uint4(TR::kOne, 0u, 0u, 0u);
+  }
+  __syncthreads();
+
+  // ---- scores, tile t: keys 16 t + 4G + i, query q0 + li; the K operand
+  // from LDS (lanes past d in the last step: zeros, whatever lies there)
+  // Every K operand is read before the first product (no load among the
+  // products, as in the per-wave form).
+  s8v ka[TPW][KS];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      ka[t][ks] = *(const s8v*)(ks_ + (16 * t + li) * PK + 32 * ks + 8 * G);
+      if (ks == KS - 1 && padlane) ka[t][ks] = (s8v){0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  __builtin_amdgcn_sched_barrier(0);
+  f4v sc[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    sc[t] = (f4v){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) sc[t] = TR::mma16(ka[t][ks], qf[ks], sc[t]);
+  }
+  // keys past Nk: -inf, by selects without a branch (as in the per-wave form)
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[t][i] = 16 * t + 4 * G + i < Nk ? sc[t][i] : -INFINITY;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+    mx = __builtin_fmaxf(__builtin_fmaxf(mx, __builtin_fmaxf(sc[t][0], sc[t][1])), __builtin_fmaxf(sc[t][2], sc[t][3]));
+  const float M2 = row16_max(mx) * c;  // Nk >= 1: finite
+  float lv = 0.f;
+  uint32_t pp[TPW + 1][2];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][i], c, -M2));
+    if constexpr (kValuSum) lv += (p[0] + p[1]) + (p[2] + p[3]);
+    pp[t][0] = TR::pack2(p[0], p[1]);
+    pp[t][1] = TR::pack2(p[2], p[3]);
+  }
+  pp[TPW][0] = pp[TPW][1] = 0u;
+
+  // ---- O^T += V^T P^T
+  f4v o[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) o[mt] = (f4v){0.f, 0.f, 0.f, 0.f};
+  // (every V operand read before the first product: no load among them)
+  const uint16_t* const va = vs_ + (4 * G + (li >> 2)) * PV + 4 * (li & 3);
+  s8v vop[(TPW + 1) / 2][MT];
+#pragma unroll
+  for (int j = 0; j < (TPW + 1) / 2; ++j)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const s4v v0 = lds_read_tr16(va + 32 * j * PV + 16 * mt);
+      const s4v v1 = lds_read_tr16(va + (32 * j + 16) * PV + 16 * mt);
+      vop[j][mt] = (s8v){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < (TPW + 1) / 2; ++j) {
+    const s8v pb = __builtin_bit_cast(s8v, (uint4){pp[2 * j][0], pp[2 * j][1], pp[2 * j + 1][0], pp[2 * j + 1][1]});
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) o[mt] = TR::mma16(vop[j][mt], pb, o[mt]);
+  }
+  float lnorm;
+  if constexpr (kValuSum) lv = row16_sum(lv);
+  if constexpr (S::kOnes) {
+    constexpr int GL = (D % 16) / 4, IL = D % 4;
+    lnorm = __shfl(o[MT - 1][IL], GL * 16 + li);
+  } else {
+    lnorm = lv;
+  }
+  const float lrep = kValuSum ? lv : lnorm;
+  const int row = q0 + li;
+  if (row < Nq) {
+    uint16_t* const op = out + oh + (size_t)row * lay.o.row + 4 * G;
+    const float inv = 1.f / lnorm;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if (!S::kOnes || mt < MT - 1 || 16 * mt + 4 * G < D) {
+        uint2 w;
+        w.x = TR::pack2(o[mt][0] * inv, o[mt][1] * inv);
+        w.y = TR::pack2(o[mt][2] * inv, o[mt][3] * inv);
+        *(uint2*)(op + 16 * mt) = w;
+      }
+    }
+    if (kML && G == 0) *(float2*)(ml + ((size_t)head * Nq + row) * 2) = make_float2(M2 / kLog2e, lrep);
+  }
+}
+
+template <class TR, int D, int TPW, bool kML>
+hipError_t launch_shared_k(const Problem& p) {
+  const dim3 grid((unsigned)((p.Nq + 16 * kSharedW - 1) / (16 * kSharedW)), (unsigned)p.lay.H, (unsigned)(p.BH / p.lay.H));
+  hipLaunchKernelGGL((short_shared_kernel<TR, D, TPW, kML>), grid, dim3(64 * kSharedW), 0, p.stream,
+                     (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v, (uint16_t*)p.out, p.ml, p.lay,
+                     p.Nq, p.Nk, p.scale);
+  return hipGetLastError();
+}
+
+template <class TR, int D, bool kML>
+hipError_t launch_shared_t(const Problem& p) {
+  switch ((p.Nk + 15) / 16) {
+    case 1: return launch_shared_k<TR, D, 1, kML>(p);
+    case 2: return launch_shared_k<TR, D, 2, kML>(p);
+    case 3: return launch_shared_k<TR, D, 3, kML>(p);
+    case 4: return launch_shared_k<TR, D, 4, kML>(p);
+    case 5: return launch_shared_k<TR, D, 5, kML>(p);
+    case 6: return launch_shared_k<TR, D, 6, kML>(p);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <class TR, int D, int TPW, bool kML>
 hipError_t launch_short_k(const Problem& p, int ksh) {
   const int qpw = 16 << (2 - ksh);  // queries per workgroup
@@ -349,15 +550,16 @@ hipError_t launch_short_t(const Problem& p, int cus) {
 }
 
 template <class TR, int D>
-hipError_t launch_short_d(const Problem& p, int cus) {
+hipError_t launch_short_d(const Problem& p, int cus, bool shared) {
+  if (shared) return p.ml ? launch_shared_t<TR, D, true>(p) : launch_shared_t<TR, D, false>(p);
   return p.ml ? launch_short_t<TR, D, true>(p, cus) : launch_short_t<TR, D, false>(p, cus);
 }
 template <class TR>
-hipError_t launch_short_ty(const Problem& p, int cus) {
+hipError_t launch_short_ty(const Problem& p, int cus, bool shared) {
   switch (p.d) {
-    case 40: return launch_short_d<TR, 40>(p, cus);
-    case 80: return launch_short_d<TR, 80>(p, cus);
-    case 160: return launch_short_d<TR, 160>(p, cus);
+    case 40: return launch_short_d<TR, 40>(p, cus, shared);
+    case 80: return launch_short_d<TR, 80>(p, cus, shared);
+    case 160: return launch_short_d<TR, 160>(p, cus, shared);
     default: return hipErrorInvalidValue;
   }
 }
@@ -373,9 +575,17 @@ int short_max_keys(int d) {
   }
 }
 
+// The two forms: shared where a head has at least one full workgroup of
+// queries (16 x 8) and at most 96 keys; per wave otherwise.  ATTN_SHORT=s /
+// w forces the shared / per-wave form where the shape allows it.
 hipError_t launch_short_flash(const Problem& p, int cus) {
   if (p.Nk < 1 || p.Nk > short_max_keys(p.d) || p.lay.H > 65535 || p.BH / p.lay.H > 65535) return hipErrorInvalidValue;
-  return p.dt == ATTN_BF16 ? launch_short_ty<BF16>(p, cus) : launch_short_ty<F16>(p, cus);
+  const bool can_share = p.Nk <= 16 * kSharedTiles;
+  bool shared = can_share && p.Nq >= 16 * kSharedW;
+  const char* e = std::getenv("ATTN_SHORT");
+  if (e && e[0] == 's') shared = can_share;
+  if (e && e[0] == 'w') shared = false;
+  return p.dt == ATTN_BF16 ? launch_short_ty<BF16>(p, cus, shared) : launch_short_ty<F16>(p, cus, shared);
 }
 
 }  // namespace attn

@@ -85,6 +85,17 @@ __device__ __forceinline__ float pmax_halves(uint32_t a) {
   return (float)__builtin_elementwise_maximum(v[0], v[1]);
 }
 
+// An MFMA result, copied after 16 wait states: for its first read after code
+// that branches.  The compiler counts the wait states such a read needs after
+// the MFMA along one of the paths into the reading block only; 16 of its own,
+// then a copy, cover every path (a 32x32x16 result read too early on the
+// other path is stale).
+__device__ __forceinline__ float mfma_settled(float x) {
+  float y;
+  asm volatile("s_nop 7\n\ts_nop 7\n\tv_mov_b32 %0, %1" : "=v"(y) : "v"(x));
+  return y;
+}
+
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their no-wait maxima)
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

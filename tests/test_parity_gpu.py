@@ -134,23 +134,31 @@ def test_fa40_kernel_forced_on_ragged_shapes(shape, dtype, monkeypatch):
 
 
 # The short-key-range kernel of attn_short.hip takes every single pass with
-# Nk <= 384 (d = 40) or <= 256 (d = 80, 160).  Its key splits per workgroup
-# (1, 2 or 4) and 16-key tiles per wave follow from the shape: these cover one
-# key, partial 16-key tiles, an odd tile count (a half-empty PV step), a split
-# left without keys, the longest ranges, query tiles past Nq, and grids large
-# enough to keep one split.
+# Nk <= 384 (d = 40) or <= 256 (d = 80, 160).  Its per-wave form (each wave
+# loads its own keys) picks key splits per workgroup (1, 2 or 4) and 16-key
+# tiles per wave from the shape; its shared form (K and V staged once per
+# workgroup of 8 waves) takes at most 96 keys.  These cover one key, partial
+# 16-key tiles, an odd tile count (a half-empty PV step), a split left
+# without keys, the longest ranges, query tiles past Nq, and grids large
+# enough to keep one split; each form is also forced (ATTN_SHORT=w / s).
 SHORT = [(1, 1, 1, 1, 40), (1, 2, 5, 3, 40), (2, 3, 77, 77, 40), (1, 2, 200, 97, 40),
          (1, 1, 64, 384, 40), (2, 8, 1000, 77, 40), (1, 2, 17, 256, 80), (2, 1, 100, 129, 80),
          (2, 8, 1000, 50, 80), (1, 1, 1, 1, 160), (1, 3, 33, 31, 160), (2, 2, 100, 65, 160),
-         (1, 1, 48, 256, 160), (1, 2, 1000, 16, 160), (2, 8, 300, 200, 160)]
+         (1, 1, 48, 256, 160), (1, 2, 1000, 16, 160), (2, 8, 300, 200, 160), (1, 2, 300, 96, 160)]
 
 
 @pytest.mark.parametrize("shape", SHORT, ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_short_kernel_on_ragged_shapes(shape, dtype, monkeypatch):
-    monkeypatch.delenv("ATTN_SHORT", raising=False)
-    monkeypatch.delenv("ATTN_FA40", raising=False)
+@pytest.mark.parametrize("form", ["auto", "w", "s"])
+def test_short_kernel_on_ragged_shapes(shape, dtype, form, monkeypatch):
     B, H, Nq, Nk, d = shape
+    if form == "s" and Nk > 96:
+        pytest.skip("the shared form takes at most 96 keys")
+    monkeypatch.delenv("ATTN_FA40", raising=False)
+    if form == "auto":
+        monkeypatch.delenv("ATTN_SHORT", raising=False)
+    else:
+        monkeypatch.setenv("ATTN_SHORT", form)
     cfg = Config(f"short_{'x'.join(map(str, shape))}", 110 + sum(shape), B, H, Nq, Nk, d, dtype)
     _run_all(cfg, dtype)
 
