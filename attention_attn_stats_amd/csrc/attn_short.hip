@@ -326,21 +326,25 @@ __global__ __launch_bounds__(256) void short_kernel(const uint16_t* __restrict__
 }
 
 // Shared form, for many queries per head over at most 96 keys (the text
-// cross-attention): the workgroup's SW waves (16 queries each, all keys)
-// stage K and V once in LDS and share them; a wave that loaded its own
-// copies would send the same bytes through the CU's load path once per 16
-// queries.  Grid: x = block of 16 SW queries, y = head in batch, z = batch.
+// cross-attention): the workgroup's 8 waves (QPW groups of 16 queries each,
+// all keys) stage K and V once in LDS and share them; a wave that loaded its
+// own copies would send the same bytes through the CU's load path once per
+// 16 queries.  A wave's K and V operands serve all its query groups, and its
+// fixed work (addressing, reductions) is spread over them.  Grid: x = block
+// of 16 QPW 8 queries, y = head in batch, z = batch.
 constexpr int kSharedW = 8;                 // waves per workgroup
 constexpr int kSharedTiles = 6;             // most 16-key tiles (96 keys)
 template <int D>
 constexpr int shared_pk() { return D == 40 ? 40 : D + 8; }  // K row pitch: 16 rows per ds_read_b128 in distinct banks
+template <int D>
+constexpr int shared_qpw() { return D == 40 ? 2 : 1; }      // query groups per wave (registers allow two at d = 40)
 
 template <class TR, int D, int TPW, bool kML>
 __global__ __launch_bounds__(64 * kSharedW) void short_shared_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ out, float* __restrict__ ml, const Layout lay, int Nq, int Nk, float scale) {
   using S = ShortShape<D>;
-  constexpr int KS = S::KS, MT = S::MT, PV = S::PV, VCH = S::VCH, PK = shared_pk<D>();
+  constexpr int KS = S::KS, MT = S::MT, PV = S::PV, VCH = S::VCH, PK = shared_pk<D>(), QPW = shared_qpw<D>();
   constexpr int W = kSharedW, T = 64 * W;
   constexpr int KROWS = 16 * TPW, VROWS = S::vrows(TPW);
   constexpr bool kValuSum = !S::kOnes || (kML && !TR::kRoundedSumOk);
@@ -355,7 +359,7 @@ __global__ __launch_bounds__(64 * kSharedW) void short_shared_kernel(
   const int head = blockIdx.z * lay.H + blockIdx.y;
   const long long qh = blockIdx.z * lay.q.batch + blockIdx.y * lay.q.head, kh = blockIdx.z * lay.k.batch + blockIdx.y * lay.k.head;
   const long long vh = blockIdx.z * lay.v.batch + blockIdx.y * lay.v.head, oh = blockIdx.z * lay.o.batch + blockIdx.y * lay.o.head;
-  const int q0 = ((int)blockIdx.x * W + wave) * 16;
+  const int q0 = ((int)blockIdx.x * W + wave) * 16 * QPW;  // query group g: rows q0 + 16 g + li
   const float c = scale * kLog2e;
   const int qrs = lay.q.row, krs = lay.k.row, vrs = lay.v.row;
   const bool padlane = S::kPadQK && 32 * (KS - 1) + 8 * G >= D;
@@ -365,10 +369,13 @@ __global__ __launch_bounds__(64 * kSharedW) void short_shared_kernel(
   // past Nk read as zero
   const __amdgpu_buffer_rsrc_t qr = make_rsrc(q + qh, ((unsigned)(Nq - 1) * (unsigned)qrs + D) * 2u);
   const unsigned qoff = ((unsigned)(q0 + li) * (unsigned)qrs + 8 * G) * 2u;
-  s8v qf[KS];
+  s8v qf[QPW][KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    qf[ks] = __builtin_bit_cast(s8v, load16(qr, (ks == KS - 1 && padlane) ? kNone : (int)(qoff + 64 * ks)));
+  for (int g = 0; g < QPW; ++g)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[g][ks] = __builtin_bit_cast(
+          s8v, load16(qr, (ks == KS - 1 && padlane) ? kNone : (int)(qoff + (unsigned)(16 * g) * (unsigned)qrs * 2u + 64 * ks)));
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + kh, ((unsigned)(Nk - 1) * (unsigned)krs + D) * 2u);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + vh, ((unsigned)(Nk - 1) * (unsigned)vrs + D) * 2u);
   constexpr int KJ = (KROWS * VCH + T - 1) / T, VJ = (VROWS * VCH + T - 1) / T;
@@ -400,10 +407,10 @@ __global__ __launch_bounds__(64 * kSharedW) void short_shared_kernel(
   }
   __syncthreads();
 
-  // ---- scores, tile t: keys 16 t + 4G + i, query q0 + li; the K operand
-  // from LDS (lanes past d in the last step: zeros, whatever lies there)
-  // Every K operand is read before the first product (no load among the
-  // products, as in the per-wave form).
+  // ---- scores, tile t: keys 16 t + 4G + i, query q0 + 16 g + li; the K
+  // operands from LDS (lanes past d in the last step: zeros, whatever lies
+  // there), every one read before the first product (no load among the
+  // products, as in the per-wave form)
   s8v ka[TPW][KS];
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
@@ -413,41 +420,46 @@ __global__ __launch_bounds__(64 * kSharedW) void short_shared_kernel(
       if (ks == KS - 1 && padlane) ka[t][ks] = (s8v){0, 0, 0, 0, 0, 0, 0, 0};
     }
   __builtin_amdgcn_sched_barrier(0);
-  f4v sc[TPW];
+  f4v sc[QPW][TPW];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    sc[t] = (f4v){0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < QPW; ++g)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) sc[t] = TR::mma16(ka[t][ks], qf[ks], sc[t]);
-  }
+    for (int t = 0; t < TPW; ++t) {
+      sc[g][t] = (f4v){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sc[g][t] = TR::mma16(ka[t][ks], qf[g][ks], sc[g][t]);
+    }
   // keys past Nk: -inf, by selects without a branch (as in the per-wave form)
 #pragma unroll
-  for (int t = 0; t < TPW; ++t)
+  for (int g = 0; g < QPW; ++g)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc[t][i] = 16 * t + 4 * G + i < Nk ? sc[t][i] : -INFINITY;
-  float mx = -INFINITY;
+    for (int t = 0; t < TPW; ++t)
 #pragma unroll
-  for (int t = 0; t < TPW; ++t)
-    mx = __builtin_fmaxf(__builtin_fmaxf(mx, __builtin_fmaxf(sc[t][0], sc[t][1])), __builtin_fmaxf(sc[t][2], sc[t][3]));
-  const float M2 = row16_max(mx) * c;  // Nk >= 1: finite
-  float lv = 0.f;
-  uint32_t pp[TPW + 1][2];
+      for (int i = 0; i < 4; ++i) sc[g][t][i] = 16 * t + 4 * G + i < Nk ? sc[g][t][i] : -INFINITY;
+  float M2[QPW], lv[QPW];
+  uint32_t pp[QPW][TPW + 1][2];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    float p[4];
+  for (int g = 0; g < QPW; ++g) {
+    float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][i], c, -M2));
-    if constexpr (kValuSum) lv += (p[0] + p[1]) + (p[2] + p[3]);
-    pp[t][0] = TR::pack2(p[0], p[1]);
-    pp[t][1] = TR::pack2(p[2], p[3]);
+    for (int t = 0; t < TPW; ++t)
+      mx = __builtin_fmaxf(__builtin_fmaxf(mx, __builtin_fmaxf(sc[g][t][0], sc[g][t][1])),
+                           __builtin_fmaxf(sc[g][t][2], sc[g][t][3]));
+    M2[g] = row16_max(mx) * c;  // Nk >= 1: finite
+    lv[g] = 0.f;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[g][t][i], c, -M2[g]));
+      if constexpr (kValuSum) lv[g] += (p[0] + p[1]) + (p[2] + p[3]);
+      pp[g][t][0] = TR::pack2(p[0], p[1]);
+      pp[g][t][1] = TR::pack2(p[2], p[3]);
+    }
+    pp[g][TPW][0] = pp[g][TPW][1] = 0u;
   }
-  pp[TPW][0] = pp[TPW][1] = 0u;
 
-  // ---- O^T += V^T P^T
-  f4v o[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) o[mt] = (f4v){0.f, 0.f, 0.f, 0.f};
-  // (every V operand read before the first product: no load among them)
+  // ---- O^T += V^T P^T (every V operand read before the first product)
   const uint16_t* const va = vs_ + (4 * G + (li >> 2)) * PV + 4 * (li & 3);
   s8v vop[(TPW + 1) / 2][MT];
 #pragma unroll
@@ -459,41 +471,53 @@ __global__ __launch_bounds__(64 * kSharedW) void short_shared_kernel(
       vop[j][mt] = (s8v){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
     }
   __builtin_amdgcn_sched_barrier(0);
+  f4v o[QPW][MT];
 #pragma unroll
-  for (int j = 0; j < (TPW + 1) / 2; ++j) {
-    const s8v pb = __builtin_bit_cast(s8v, (uint4){pp[2 * j][0], pp[2 * j][1], pp[2 * j + 1][0], pp[2 * j + 1][1]});
+  for (int g = 0; g < QPW; ++g)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) o[mt] = TR::mma16(vop[j][mt], pb, o[mt]);
-  }
-  float lnorm;
-  if constexpr (kValuSum) lv = row16_sum(lv);
-  if constexpr (S::kOnes) {
-    constexpr int GL = (D % 16) / 4, IL = D % 4;
-    lnorm = __shfl(o[MT - 1][IL], GL * 16 + li);
-  } else {
-    lnorm = lv;
-  }
-  const float lrep = kValuSum ? lv : lnorm;
-  const int row = q0 + li;
-  if (row < Nq) {
-    uint16_t* const op = out + oh + (size_t)row * lay.o.row + 4 * G;
-    const float inv = 1.f / lnorm;
+    for (int mt = 0; mt < MT; ++mt) o[g][mt] = (f4v){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      if (!S::kOnes || mt < MT - 1 || 16 * mt + 4 * G < D) {
-        uint2 w;
-        w.x = TR::pack2(o[mt][0] * inv, o[mt][1] * inv);
-        w.y = TR::pack2(o[mt][2] * inv, o[mt][3] * inv);
-        *(uint2*)(op + 16 * mt) = w;
-      }
+  for (int j = 0; j < (TPW + 1) / 2; ++j)
+#pragma unroll
+    for (int g = 0; g < QPW; ++g) {
+      const s8v pb =
+          __builtin_bit_cast(s8v, (uint4){pp[g][2 * j][0], pp[g][2 * j][1], pp[g][2 * j + 1][0], pp[g][2 * j + 1][1]});
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) o[g][mt] = TR::mma16(vop[j][mt], pb, o[g][mt]);
     }
-    if (kML && G == 0) *(float2*)(ml + ((size_t)head * Nq + row) * 2) = make_float2(M2 / kLog2e, lrep);
+#pragma unroll
+  for (int g = 0; g < QPW; ++g) {
+    float lnorm;
+    if constexpr (kValuSum) lv[g] = row16_sum(lv[g]);
+    if constexpr (S::kOnes) {
+      constexpr int GL = (D % 16) / 4, IL = D % 4;
+      lnorm = __shfl(o[g][MT - 1][IL], GL * 16 + li);
+    } else {
+      lnorm = lv[g];
+    }
+    const float lrep = kValuSum ? lv[g] : lnorm;
+    const int row = q0 + 16 * g + li;
+    if (row < Nq) {
+      uint16_t* const op = out + oh + (size_t)row * lay.o.row + 4 * G;
+      const float inv = 1.f / lnorm;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (!S::kOnes || mt < MT - 1 || 16 * mt + 4 * G < D) {
+          uint2 w;
+          w.x = TR::pack2(o[g][mt][0] * inv, o[g][mt][1] * inv);
+          w.y = TR::pack2(o[g][mt][2] * inv, o[g][mt][3] * inv);
+          *(uint2*)(op + 16 * mt) = w;
+        }
+      }
+      if (kML && G == 0) *(float2*)(ml + ((size_t)head * Nq + row) * 2) = make_float2(M2[g] / kLog2e, lrep);
+    }
   }
 }
 
 template <class TR, int D, int TPW, bool kML>
 hipError_t launch_shared_k(const Problem& p) {
-  const dim3 grid((unsigned)((p.Nq + 16 * kSharedW - 1) / (16 * kSharedW)), (unsigned)p.lay.H, (unsigned)(p.BH / p.lay.H));
+  constexpr int qwg = 16 * shared_qpw<D>() * kSharedW;  // queries per workgroup
+  const dim3 grid((unsigned)((p.Nq + qwg - 1) / qwg), (unsigned)p.lay.H, (unsigned)(p.BH / p.lay.H));
   hipLaunchKernelGGL((short_shared_kernel<TR, D, TPW, kML>), grid, dim3(64 * kSharedW), 0, p.stream,
                      (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v, (uint16_t*)p.out, p.ml, p.lay,
                      p.Nq, p.Nk, p.scale);
@@ -575,8 +599,8 @@ int short_max_keys(int d) {
   }
 }
 
-// The two forms: shared where a head has at least one full workgroup of
-// queries (16 x 8) and at most 96 keys; per wave otherwise.  ATTN_SHORT=s /
+// The two forms: shared where a head has at least one full workgroup's worth
+// of 16-query groups (8) and at most 96 keys; per wave otherwise.  ATTN_SHORT=s /
 // w forces the shared / per-wave form where the shape allows it.
 hipError_t launch_short_flash(const Problem& p, int cus) {
   if (p.Nk < 1 || p.Nk > short_max_keys(p.d) || p.lay.H > 65535 || p.BH / p.lay.H > 65535) return hipErrorInvalidValue;
