@@ -91,10 +91,10 @@ __device__ __forceinline__ float row16_sum(float x) {
 // indexes by is wave-uniform scalar work, and its loads, LDS accesses and
 // stores use one per-lane address each plus immediate offsets: with so little
 // work per wave, the count of instructions it issues sets the time.
-template <class TR, int D, int TPW, bool kML>
+template <class TR, int D, int TPW, int KSPL, bool kML>
 __global__ __launch_bounds__(256) void short_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                     const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
-                                                    float* __restrict__ ml, const Layout lay, int Nq, int Nk, int ksh,
+                                                    float* __restrict__ ml, const Layout lay, int Nq, int Nk,
                                                     float scale) {
   using S = ShortShape<D>;
   constexpr int KS = S::KS, MT = S::MT, PV = S::PV, VCH = S::VCH;
@@ -108,7 +108,8 @@ __global__ __launch_bounds__(256) void short_kernel(const uint16_t* __restrict__
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = lane >> 4, li = lane & 15;
-  const int kspl = 1 << ksh;
+  constexpr int kspl = KSPL, ksh = KSPL == 4 ? 2 : (KSPL == 2 ? 1 : 0);
+  static_assert(KSPL == 1 || KSPL == 2 || KSPL == 4, "key splits: 1, 2 or 4");
   const int split = wave & (kspl - 1), qg = wave >> ksh;
   const int head = blockIdx.z * lay.H + blockIdx.y;  // batch-major head index (of ml)
   const long long qh = blockIdx.z * lay.q.batch + blockIdx.y * lay.q.head, kh = blockIdx.z * lay.k.batch + blockIdx.y * lay.k.head;
@@ -271,8 +272,8 @@ __global__ __launch_bounds__(256) void short_kernel(const uint16_t* __restrict__
     if (kML && G == 0 && rowok) *(float2*)(ml + ((size_t)head * Nq + row) * 2) = make_float2(m2 / kLog2e, l);
   };
 
-  if (ksh == 0) {
-    const float inv = 1.f / lnorm;
+  if constexpr (KSPL == 1) {
+    const float inv = __builtin_amdgcn_rcpf(lnorm);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) store_tile(mt, o[mt], inv);
     store_ml(M2, lrep);
@@ -309,7 +310,7 @@ __global__ __launch_bounds__(256) void short_kernel(const uint16_t* __restrict__
       Lr = __builtin_fmaf(xt[MT * 256 + 32 + li], f[t], Lr);
     }
   }
-  const float inv = 1.f / L;
+  const float inv = __builtin_amdgcn_rcpf(L);
   for (int mt = split; mt < MT; mt += kspl) {
     f4v acc = (f4v){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -499,7 +500,7 @@ __global__ __launch_bounds__(64 * kSharedW) void short_shared_kernel(
     const int row = q0 + 16 * g + li;
     if (row < Nq) {
       uint16_t* const op = out + oh + (size_t)row * lay.o.row + 4 * G;
-      const float inv = 1.f / lnorm;
+      const float inv = __builtin_amdgcn_rcpf(lnorm);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if (!S::kOnes || mt < MT - 1 || 16 * mt + 4 * G < D) {
@@ -537,14 +538,23 @@ hipError_t launch_shared_t(const Problem& p) {
   }
 }
 
+template <class TR, int D, int TPW, int KSPL, bool kML>
+hipError_t launch_short_kk(const Problem& p) {
+  constexpr int qwg = 16 * (ShortShape<D>::W / KSPL);  // queries per workgroup
+  const dim3 grid((unsigned)((p.Nq + qwg - 1) / qwg), (unsigned)p.lay.H, (unsigned)(p.BH / p.lay.H));
+  hipLaunchKernelGGL((short_kernel<TR, D, TPW, KSPL, kML>), grid, dim3(64 * ShortShape<D>::W), 0, p.stream,
+                     (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v, (uint16_t*)p.out, p.ml, p.lay,
+                     p.Nq, p.Nk, p.scale);
+  return hipGetLastError();
+}
 template <class TR, int D, int TPW, bool kML>
 hipError_t launch_short_k(const Problem& p, int ksh) {
-  const int qpw = 16 << (2 - ksh);  // queries per workgroup
-  const dim3 grid((unsigned)((p.Nq + qpw - 1) / qpw), (unsigned)p.lay.H, (unsigned)(p.BH / p.lay.H));
-  hipLaunchKernelGGL((short_kernel<TR, D, TPW, kML>), grid, dim3(64 * ShortShape<D>::W), 0, p.stream,
-                     (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v, (uint16_t*)p.out, p.ml, p.lay,
-                     p.Nq, p.Nk, ksh, p.scale);
-  return hipGetLastError();
+  switch (ksh) {
+    case 0: return launch_short_kk<TR, D, TPW, 1, kML>(p);
+    case 1: return launch_short_kk<TR, D, TPW, 2, kML>(p);
+    case 2: return launch_short_kk<TR, D, TPW, 4, kML>(p);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <class TR, int D, bool kML>
