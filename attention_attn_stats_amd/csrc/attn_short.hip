@@ -144,22 +144,30 @@ __global__ __launch_bounds__(256) void short_kernel(const uint16_t* __restrict__
     for (int ks = 0; ks < KS; ++ks)
       kf[t][ks] = __builtin_bit_cast(
           s8v, load16(kr, (ks == KS - 1 && padlane) ? kNone : (int)(koff + (unsigned)(32 * t) * (unsigned)krs + 64 * ks)));
-  // V rows of the block: LPR lanes per row, rows lane / LPR of each block
-  // of RPI = 64 / LPR rows, 16-byte chunks lane % LPR + LPR c; rows past the
-  // wave's tiles or past Nk as zeros (their P are zero, and 0 * a stale
-  // non-finite LDS value would not be)
-  constexpr int LPR = VCH % 4 == 0 ? 4 : (VCH % 2 == 0 ? 2 : 1);
-  constexpr int RPI = 64 / LPR, CPL = VCH / LPR;
-  constexpr int DROWS = 16 * TPW, NRB = (DROWS + RPI - 1) / RPI;  // rows with data, their row blocks
-  constexpr int ZRB = (VROWS + RPI - 1) / RPI - NRB;              // row blocks of zeros only
-  const int vr0 = lane / LPR;
-  const unsigned voff = ((unsigned)vr0 * (unsigned)vrs + 8 * (lane % LPR)) * 2u;
-  uint4 stg[NRB][CPL];
+  // V rows of the block, as 16-byte chunks in row-major order: load j takes
+  // chunks 64 j .. 64 j + 63, one contiguous kilobyte of a dense tensor (the
+  // fastest pattern for a CU's load path).  Five loads cover RB = 320 / VCH
+  // rows, so a lane's (row, chunk) of load 5 m + n is (R_n + RB m, C_n).
+  // Rows past the wave's tiles or past Nk read as zeros (their P are zero,
+  // and 0 * a stale non-finite LDS value would not be).
+  constexpr int RB = 320 / VCH, DROWS = 16 * TPW;
+  constexpr int VJ = (DROWS * VCH + 63) / 64;  // loads with data
+  static_assert(320 % VCH == 0, "five loads cover whole rows");
+  int vgo[5], vlo[5], vrn[5];                   // global byte offset, LDS element offset, row of load n
 #pragma unroll
-  for (int b = 0; b < NRB; ++b) {
-    const int off = RPI * b + vr0 < DROWS ? (int)(voff + (unsigned)(RPI * b) * (unsigned)vrs * 2u) : kNone;
+  for (int n = 0; n < 5; ++n) {
+    const int idx = 64 * n + lane, r = idx / VCH, col = idx - r * VCH;
+    vrn[n] = r;
+    vgo[n] = (int)(((unsigned)r * (unsigned)vrs + 8 * col) * 2u);
+    vlo[n] = r * PV + 8 * col;
+  }
+  uint4 stg[VJ];
 #pragma unroll
-    for (int col = 0; col < CPL; ++col) stg[b][col] = load16(vr, off + 16 * LPR * col);
+  for (int j = 0; j < VJ; ++j) {
+    const int n = j % 5, m = j / 5;
+    const bool whole = RB * m + RB <= DROWS;  // every row of this period has data
+    const int off = vgo[n] + (int)((unsigned)(RB * m) * (unsigned)vrs * 2u);
+    stg[j] = load16(vr, whole || vrn[n] + RB * m < DROWS ? off : kNone);
   }
 
   // No load is issued once the products have started: a load landing in a
@@ -204,22 +212,25 @@ __global__ __launch_bounds__(256) void short_kernel(const uint16_t* __restrict__
   }
   pp[TPW][0] = pp[TPW][1] = 0u;
 
-  // ---- V block into this wave's LDS region (only this wave reads it)
+  // ---- V block into this wave's LDS region (only this wave reads it); rows
+  // DROWS .. VROWS - 1 (an odd tile count) as zeros
   uint16_t* const vs = (uint16_t*)(smem + wave * REGION);
-  {
-    uint16_t* const vw = vs + vr0 * PV + 8 * (lane % LPR);
 #pragma unroll
-    for (int b = 0; b < NRB + ZRB; ++b) {
-      if (RPI * b + RPI <= VROWS || RPI * b + vr0 < VROWS) {
+  for (int j = 0; j < VJ; ++j) {
+    const int n = j % 5, m = j / 5;
+    if (RB * m + RB <= VROWS || vrn[n] + RB * m < VROWS) *(uint4*)(vs + vlo[n] + RB * m * PV) = stg[j];
+  }
+  if constexpr (VROWS > DROWS) {
+    constexpr int ZCH = (VROWS - DROWS) * VCH;  // chunks of zero rows
 #pragma unroll
-        for (int col = 0; col < CPL; ++col)
-          *(uint4*)(vw + RPI * b * PV + 8 * LPR * col) = b < NRB ? stg[b < NRB ? b : 0][col] : make_uint4(0u, 0u, 0u, 0u);
-      }
+    for (int z = lane; z < ZCH; z += 64) {
+      const int r = DROWS + z / VCH, col = z - (z / VCH) * VCH;
+      *(uint4*)(vs + r * PV + 8 * col) = make_uint4(0u, 0u, 0u, 0u);
     }
-    // columns D .. PV-1: 1.0 in column D (the row-sum dim), zeros after it
-    if constexpr (S::kOnes) {
-      for (int r = lane; r < VROWS; r += 64) *(uint4*)(vs + r * PV + D) = make_uint4(TR::kOne, 0u, 0u, 0u);
-    }
+  }
+  // columns D .. PV-1: 1.0 in column D (the row-sum dim), zeros after it
+  if constexpr (S::kOnes) {
+    for (int r = lane; r < VROWS; r += 64) *(uint4*)(vs + r * PV + D) = make_uint4(TR::kOne, 0u, 0u, 0u);
   }
   // (a wave's LDS operations complete in order: its reads below see its writes)
 
