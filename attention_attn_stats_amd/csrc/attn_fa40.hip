@@ -9,13 +9,14 @@
 // from the row statistics of the first pass).
 //
 // Design for gfx950 (one wave = 32 queries; 16 waves per CU):
-//  * Both products on v_mfma_f32_32x32x16: S^T = K Q^T (a 32-key tile, the
-//    head dim in three K=16 steps) and O^T += V^T P^T (two 32-row tiles of
-//    O^T: dims 0-31, and dims 32-39 plus the row sum).  The 32x32 result
-//    layout of S^T is the B-operand layout of the PV product once its keys
-//    are renumbered, so P goes from the exponentials straight into the
-//    product, with no cross-lane exchange; V^T comes from LDS in the same
-//    key order through ds_read_b64_tr_b16.
+//  * S^T = K Q^T on v_mfma_f32_32x32x16 (a 32-key tile, the head dim in three
+//    K=16 steps).  O^T += V^T P^T in two parts: dims 0-31 as one 32-row tile
+//    on v_mfma_f32_32x32x16, whose B-operand layout is the 32x32 result
+//    layout of S^T once its keys are renumbered (P goes from the exponentials
+//    straight into the product); dims 32-47 (dims 32-39, the row sum, zeros)
+//    as two 16x16x32 products, one per 16 queries, on P re-laid out by four
+//    v_permlane16_swap per tile (a 32-row tile there would be 23/32 padding).
+//    V^T comes from LDS in the matching key orders through ds_read_b64_tr_b16.
 //  * Row 40 of V^T is 1.0 for every key, so row 40 of O^T is the row sum l
 //    of the same rounded P the numerator used.
 //  * Each wave runs a software pipeline over 32-key tiles: while the vector
@@ -100,6 +101,17 @@ __device__ __forceinline__ void lds_store16(lds8* p, uint32_t x0, uint32_t x1, u
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, lds8* dst, int voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, voff, 0, 0, 0);
 }
+// C += A B on v_mfma_f32_16x16x32 with the accumulator kept in its registers
+// (destination = accumulator input): the LDS reads of the next tile may then
+// reuse no register the product still reads.  The two wait states cover a
+// vector-ALU write of A or B just before (the exchanged P).
+template <class TR>
+__device__ __forceinline__ void mma16_acc(s8v a, s8v b, f4v& c) {
+  if constexpr (TR::kPackedMax)
+    asm("s_nop 1\n\tv_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  else
+    asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
 __device__ __forceinline__ s4v lds_tr(const lds8* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((s4v __attribute__((address_space(3)))*)p);
 }
@@ -130,6 +142,13 @@ struct Dma {
   int voff[Cfg<QG>::MAXJ];
   bool act[Cfg<QG>::MAXJ];
 };
+
+// The row sum l of query l32 (row 40 of O^T in the 16x16 layout: register 0
+// of lanes 32-47 of the queries-0-15 tile a or the queries-16-31 tile b).
+__device__ __forceinline__ float row_sum(float a, float b, int l32) {
+  const float la = __shfl(a, 32 + (l32 & 15)), lb = __shfl(b, 32 + (l32 & 15));
+  return l32 < 16 ? la : lb;
+}
 
 }  // namespace fa40
 
@@ -219,7 +238,7 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
     }
   }
   // issue the direct loads of local block b into its slot
-  auto issue = [&](int b) {
+  auto issue = [&](int b) __attribute__((always_inline)) {
     const int key0 = (KH * b + splitu) * BN;
     const unsigned kbytes = Nk > key0 ? ((unsigned)(Nk - key0 - 1) * (unsigned)krs + D) * 2u : 0u;
     const unsigned vbytes = Nk > key0 ? ((unsigned)(Nk - key0 - 1) * (unsigned)vrs + D) * 2u : 0u;
@@ -253,43 +272,73 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
   // 16-lane group the addressing lane a names key (group key base) + a / 4 and
   // dims base + 4 (a % 4), base = 16 (group % 2) + 32 mt; the key base of a
   // read is 32 t + 16 s + 8 e + 4 hi (t tile, s K step, e half of the 8 keys)
-  int offV[2];
+  int offV;
   {
     const int a = lane & 15, gsub = (lane >> 4) & 1;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int dim = 16 * gsub + 32 * mt + 4 * (a & 3);
-      const int chunk = dim < D ? dim >> 3 : 5;
-      const int half = dim < D ? (dim >> 2) & 1 : (dim < 44 ? 0 : 1);
-      offV[mt] = KBYTES + 16 * (VGRP * hi + 4 * chunk + (a >> 2)) + 8 * half;
-    }
+    const int dim = 16 * gsub + 4 * (a & 3);
+    offV = KBYTES + 16 * (VGRP * hi + 4 * (dim >> 3) + (a >> 2)) + 8 * ((dim >> 2) & 1);
+  }
+  // V^T rows 32-47 (A operand of the 16x16x32 products): 16-lane group g
+  // holds keys base(g) + 0..3 and base(g) + 8..11 of a 32-key tile, base =
+  // 0, 16, 4, 20 (the key order of P after the swaps); addressing lane a
+  // names key base + a / 4 (+ 8 in the second read), dims 32 + 4 (a % 4):
+  // chunk 4 (dims 32-39) or chunk 5 (1.0 at dim 40, then zeros)
+  int offW;
+  {
+    const int a = lane & 15, g = lane >> 4;
+    const int grp = (g & 1) * 4 + (g >> 1);  // base / 4
+    offW = KBYTES + 16 * (VGRP * grp + 4 * (4 + ((a & 3) >> 1)) + (a >> 2)) + 8 * (a & 1);
   }
 
   // ---- building blocks of the pipeline
   // scores of tile t (0/1) of the block in slot sl: S^T, 32 keys x 32 queries
-  auto qk = [&](const lds8* sl, int t) {
+  auto qk = [&](const lds8* sl, int t) __attribute__((always_inline)) {
     const lds8* p = sl + offK + t * 32 * KPITCH;
     f16v s = TR::mma32(lds_read_b128(p), qf[0], (f16v){});
     s = TR::mma32(lds_read_b128(p + 32), qf[1], s);
     s = TR::mma32(lds_read_b128(p + 64), qf[2], s);
     return s;
   };
-  // O^T += V^T P^T over tile t of the block in slot sl (P packed: pp[2 s + i])
-  f16v o0 = (f16v){}, o1 = (f16v){};
-  auto pv = [&](const lds8* sl, int t, const uint32_t (&pp)[8]) {
+  // O^T += V^T P^T over tile t of the block in slot sl (P packed: pp[2 s + i]):
+  // dims 0-31 in o0 (32x32 layout), dims 32-47 in oa (queries 0-15) and ob
+  // (queries 16-31), 16x16 layout: lane (n, r) holds dims 32 + 4 r .. + 3 of
+  // query n (+ 16 in ob)
+  f16v o0 = (f16v){};
+  f4v oa = (f4v){}, ob = (f4v){};
+  float oscale = 1.f;  // the exact pass: factor O takes to the current reference
+  auto pv = [&](const lds8* sl, int t, const uint32_t (&pp)[8], bool exact) __attribute__((always_inline)) {
+    if (exact) {
+      // the previous tile's 16x16x32 results may still be in flight: wait
+      // them out (the compiler does not see the products as such)
+      asm volatile("s_nop 7\n\ts_nop 7" : "+v"(oa), "+v"(ob));
+      // the factor is per query l32; oa holds query lane % 16, ob 16 + lane % 16
+      const float sa = __shfl(oscale, lane & 15), sb = __shfl(oscale, 16 + (lane & 15));
+      o0 *= oscale;
+      oa *= sa;
+      ob *= sb;
+      oscale = 1.f;
+    }
+    const s4v w0 = lds_tr(sl + offW + 16 * VGRP * 8 * t), w1 = lds_tr(sl + offW + 16 * VGRP * (8 * t + 2));
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const s8v bop = __builtin_bit_cast(s8v, (uint4){pp[4 * s], pp[4 * s + 1], pp[4 * s + 2], pp[4 * s + 3]});
       const int kofs = 16 * VGRP * (8 * t + 4 * s);
-      const s4v a0 = lds_tr(sl + offV[0] + kofs), a1 = lds_tr(sl + offV[0] + kofs + 16 * VGRP * 2);
-      const s4v b0 = lds_tr(sl + offV[1] + kofs), b1 = lds_tr(sl + offV[1] + kofs + 16 * VGRP * 2);
+      const s4v a0 = lds_tr(sl + offV + kofs), a1 = lds_tr(sl + offV + kofs + 16 * VGRP * 2);
       o0 = TR::mma32((s8v){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]}, bop, o0);
-      o1 = TR::mma32((s8v){b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]}, bop, o1);
     }
+    // P re-laid out for the 16x16x32 products: x[0..3] then holds queries
+    // 0-15 and x[4..7] queries 16-31, keys base(g) + 0..3, + 8..11 per group
+    const auto r0 = __builtin_amdgcn_permlane16_swap(pp[0], pp[4], false, false);
+    const auto r1 = __builtin_amdgcn_permlane16_swap(pp[1], pp[5], false, false);
+    const auto r2 = __builtin_amdgcn_permlane16_swap(pp[2], pp[6], false, false);
+    const auto r3 = __builtin_amdgcn_permlane16_swap(pp[3], pp[7], false, false);
+    const s8v wop = (s8v){w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+    mma16_acc<TR>(wop, __builtin_bit_cast(s8v, (uint4){r0[0], r1[0], r2[0], r3[0]}), oa);
+    mma16_acc<TR>(wop, __builtin_bit_cast(s8v, (uint4){r0[1], r1[1], r2[1], r3[1]}), ob);
   };
   float mref = 0.f, mtrue = -INFINITY, lsum = 0.f;
   // P of a score tile against mref, rounded and packed (the fast path)
-  auto expo = [&](const f16v& s, uint32_t (&pp)[8]) {
+  auto expo = [&](const f16v& s, uint32_t (&pp)[8]) __attribute__((always_inline)) {
     float p[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -mref));
@@ -300,7 +349,7 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
       for (int i = 0; i < 16; ++i) lsum += p[i];
     }
   };
-  auto tile_max = [&](const f16v& s) {
+  auto tile_max = [&](const f16v& s) __attribute__((always_inline)) {
     float m = s[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) m = __builtin_fmaxf(m, s[i]);
@@ -308,11 +357,11 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
   };
   // the exact online form: move the reference to the running max first
   // (O and the fp32 sum scaled to it), then P
-  auto expo_exact = [&](const f16v& s, uint32_t (&pp)[8]) {
+  auto expo_exact = [&](const f16v& s, uint32_t (&pp)[8]) __attribute__((always_inline)) {
     const float mn = __builtin_fmaxf(mref, tile_max(s) * c);
     const float alpha = __builtin_amdgcn_exp2f(mref - mn);
-    o0 *= alpha;
-    o1 *= alpha;
+    oscale = alpha;  // O moves to the new reference in the next pv, before P of this tile
+
     lsum *= alpha;
     mref = mn;
     expo(s, pp);
@@ -325,7 +374,9 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
   // so that every test of `exact` folds away)
   auto run = [&](bool exact) __attribute__((always_inline)) {
     o0 = (f16v){};
-    o1 = (f16v){};
+    oa = (f4v){};
+    ob = (f4v){};
+    oscale = 1.f;
     lsum = 0.f;
     mtrue = -INFINITY;
     // V ones chunks and K mask chunks of every slot of this split
@@ -364,9 +415,9 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
     // one tile step: P of `cur` into `pout`, scores of the next tile into
     // `snext` (when there is one), PV of the previous tile (`pin`)
     auto step = [&](const lds8* ks, int kt, const lds8* vs, int vt, const f16v& cur, f16v& snext,
-                    const uint32_t (&pin)[8], uint32_t (&pout)[8], bool has_next) {
+                    const uint32_t (&pin)[8], uint32_t (&pout)[8], bool has_next) __attribute__((always_inline)) {
       if (has_next) snext = qk(ks, kt);
-      pv(vs, vt, pin);
+      pv(vs, vt, pin, exact);
       if (exact) {
         expo_exact(cur, pout);
       } else {
@@ -375,7 +426,7 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
       }
     };
     // full bodies: tiles 2b+1 and 2b+2, scores of block b+1, PV of block b
-    auto body = [&](int b) {
+    auto body = [&](int b) __attribute__((always_inline)) {
       const lds8* ks = ring + ((b + 1) % NBUF) * SLOT;
       const lds8* vs = ring + (b % NBUF) * SLOT;
       f16v s2;
@@ -402,7 +453,7 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
       const lds8* vs = ring + ((nb - 1) % NBUF) * SLOT;
       f16v unused;
       step(vs, 0, vs, 0, s1, unused, pa, pb, false);
-      pv(vs, 1, pb);
+      pv(vs, 1, pb, exact);
       barrier();
     }
     // a split with fewer blocks meets the other's barriers
@@ -411,9 +462,8 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
   };
 
   run(false);
-  // the row sum is row 40 of O^T: register 4 of the second tile on lanes 0-31
-  // (the loop above may end on either of two branches: mfma_settled)
-  float lrow = __shfl(mfma_settled(o1[4]), l32);
+  // the row sum (the loop above may end on either of two branches: mfma_settled)
+  float lrow = row_sum(mfma_settled(oa[0]), mfma_settled(ob[0]), l32);
   if constexpr (!kPV) {
     // a row whose sum left the fast path's range is recomputed by all waves
     if (nb > 0 && __any(!(lrow < kSumLimit))) redo_flag = 1;
@@ -422,7 +472,7 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
     if (redo_flag) {
       barrier();
       run(true);
-      lrow = __shfl(mfma_settled(o1[4]), l32);
+      lrow = row_sum(mfma_settled(oa[0]), mfma_settled(ob[0]), l32);
     }
   }
   if (nb == 0) {
@@ -430,6 +480,14 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
     mtrue = -INFINITY;
   }
   float lr = kValuSum ? pair_sum32(lsum) : lrow;
+  // dims 32 + 4 hi .. + 3 of query l32, from lane (l32 % 16) + 16 hi of oa
+  // or ob: from here on every value of a lane belongs to query l32
+  float d[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float da = __shfl(oa[i], (l32 & 15) + 16 * hi), db = __shfl(ob[i], (l32 & 15) + 16 * hi);
+    d[i] = l32 < 16 ? da : db;
+  }
 
   // ---- merge the key splits: split 1 hands (m, O, l) to split 0 through LDS
   wait_lds();
@@ -439,30 +497,32 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
     ex[0] = mref;
     ex[64] = mtrue;
     ex[128] = lr;
+    ex[192] = lrow;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ex[(3 + i) * 64] = o0[i];
+    for (int i = 0; i < 16; ++i) ex[(4 + i) * 64] = o0[i];
 #pragma unroll
-    for (int i = 0; i < 5; ++i) ex[(19 + i) * 64] = o1[i];
+    for (int i = 0; i < 4; ++i) ex[(20 + i) * 64] = d[i];
   }
   wait_lds();
   barrier();
   if (split > 0) return;
   {
-    const float mB = ex[0], mtB = ex[64], lrB = ex[128];
+    const float mB = ex[0], mtB = ex[64], lrB = ex[128], lrowB = ex[192];
     // a split that saw no key holds (-inf, 0): it contributes nothing
     const float M = kPV ? mref : __builtin_fmaxf(mref, mB);
     const float fA = kPV ? 1.f : __builtin_amdgcn_exp2f(mref - M);
     const float fB = kPV ? 1.f : __builtin_amdgcn_exp2f(mB - M);
     // explicit FMAs: the contraction of the merge is fixed
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o0[i] = __builtin_fmaf(o0[i], fA, ex[(3 + i) * 64] * fB);
+    for (int i = 0; i < 16; ++i) o0[i] = __builtin_fmaf(o0[i], fA, ex[(4 + i) * 64] * fB);
 #pragma unroll
-    for (int i = 0; i < 5; ++i) o1[i] = __builtin_fmaf(o1[i], fA, ex[(19 + i) * 64] * fB);
+    for (int i = 0; i < 4; ++i) d[i] = __builtin_fmaf(d[i], fA, ex[(20 + i) * 64] * fB);
     lr = __builtin_fmaf(lr, fA, lrB * fB);
+    lrow = __builtin_fmaf(lrow, fA, lrowB * fB);
     mtrue = __builtin_fmaxf(mtrue, mtB);
     mref = M;
   }
-  const float l = __shfl(o1[4], l32);  // the merged row sum, on both halves
+  const float l = lrow;  // the merged row sum
   const int row = qbase + l32;
   if (row >= Nq) return;
   float inv;
@@ -481,8 +541,8 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
   }
   {
     uint2 w;
-    w.x = TR::pack2(o1[0] * inv, o1[1] * inv);
-    w.y = TR::pack2(o1[2] * inv, o1[3] * inv);
+    w.x = TR::pack2(d[0] * inv, d[1] * inv);
+    w.y = TR::pack2(d[2] * inv, d[3] * inv);
     *(uint2*)(op + 32 + 4 * hi) = w;
   }
   if constexpr (kML) {
