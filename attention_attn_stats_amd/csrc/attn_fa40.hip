@@ -388,14 +388,15 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
     }
     wait_lds();
     barrier();  // the chunks are written before any direct load of the pass lands next to them
-    const int npre = nb < NBUF ? nb : NBUF;
-    for (int b = 0; b < npre; ++b) issue(b);
-    // blocks 0 and 1 must have landed; blocks 2 and 3 may still be in flight
-    if (npre >= 4) wait_vm<2 * C::MAXJ>();
-    else if (npre == 3) wait_vm<C::MAXJ>();
-    else wait_vm<0>();
+    // blocks 0 and 1 land before the pass starts; blocks 2 and 3 are issued
+    // only then (with every workgroup of the chip starting at once, the
+    // first blocks would otherwise queue behind twice the bytes)
+    const int npre = nb < NBUF ? nb : NBUF, nfirst = npre < 2 ? npre : 2;
+    for (int b = 0; b < nfirst; ++b) issue(b);
+    wait_vm<0>();
     wait_lds();
     barrier();
+    for (int b = nfirst; b < npre; ++b) issue(b);
 
     uint32_t pa[8], pb[8];
     f16v s1 = (f16v){};
