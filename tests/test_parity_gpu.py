@@ -133,6 +133,22 @@ def test_fa40_kernel_forced_on_ragged_shapes(shape, dtype, monkeypatch):
     _run_all(cfg, dtype)
 
 
+# Around the default dispatch boundary of the head-dimension-40 kernel (more
+# than 1024 keys, every workgroup resident): the general kernel at 1024 keys,
+# the attn_fa40.hip kernel from 1025 on (a one-key last block, a partial one,
+# an odd block count that leaves the two key splits uneven).
+FA40_BOUNDARY = [(1, 2, 300, 1024), (1, 2, 300, 1025), (2, 1, 257, 1500), (1, 1, 64, 1088)]
+
+
+@pytest.mark.parametrize("shape", FA40_BOUNDARY, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_fa40_dispatch_boundary(shape, dtype, monkeypatch):
+    monkeypatch.delenv("ATTN_FA40", raising=False)
+    B, H, Nq, Nk = shape
+    cfg = Config(f"fa40b_{'x'.join(map(str, shape))}", 90 + sum(shape), B, H, Nq, Nk, 40, dtype)
+    _run_all(cfg, dtype)
+
+
 # The short-key-range kernel of attn_short.hip takes every single pass with
 # Nk <= 384 (d = 40) or <= 256 (d = 80, 160).  Its per-wave form (each wave
 # loads its own keys) picks key splits per workgroup (1, 2 or 4) and 16-key
