@@ -70,6 +70,16 @@ constexpr int DUMMY = 2 * RING;                   // 1 KB that out-of-range padd
 // a row whose fast-path sum is not below this is recomputed (P up to
 // 65504 per key in fp16; bf16 P never overflows, the bound keeps O finite)
 constexpr float kSumLimit = 1125899906842624.f;   // 2^50
+// fp16 fast path: the reference max lies this far (exp2 units) above the
+// first tile's max.  A later score more than 16 above the reference makes P
+// leave the fp16 range and the whole workgroup redo its rows; with logits of
+// standard deviation ~2.25 (Q, K ~ N(0, 1.5^2) at d = 40) a 16-unit gap above
+// the first 32 keys' max occurs in a few rows of a 4096 x 4096 launch, and one
+// such row doubles its workgroup's time.  At 4 the gap needed is 20; the
+// first tile's max key weighs 2^-4, a P stays in the fp16 normal range down to
+// 2^-14 (keys 10 below that max), and each one rounded in the denormal range
+// errs by at most 2^-25, i.e. 2^-21 of the row sum.
+constexpr float kHeadroom = 4.f;
 
 template <int QG>
 struct Cfg {
@@ -407,10 +417,13 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
         const int row = qbase + l32;
         mref = row < Nq ? ml[((size_t)head * Nq + row) * 2] * kLog2e : 0.f;
       } else {
-        mref = tile_max(s0) * c;
+        const float m0 = tile_max(s0) * c;
+        // fp16 P: the reference sits kHeadroom above the first tile's max, so
+        // that scores up to 16 + kHeadroom above it stay finite
+        mref = (!exact && TR::kPackedMax) ? m0 + kHeadroom : m0;
+        if (exact || kML) mtrue = m0;
       }
       s1 = qk(ring, 1);
-      if (exact || kML) mtrue = mref;
       expo(s0, pa);
     }
     // one tile step: P of `cur` into `pout`, scores of the next tile into
