@@ -590,19 +590,18 @@ hipError_t by_type(const Problem& p) {
 }
 
 // Whether a head-dimension-40 problem takes the kernel of attn_fa40.hip or
-// this file's.  Measured on MI355X (both kernels in one process, B=2, H=8,
-// per-launch medians): where all its workgroups are resident at once (one
-// 256-query workgroup per CU; Nq = 4096) the attn_fa40.hip kernel is 4-8 %
-// faster from 1536 keys on (Nq = 4096: 1536-16384 keys), level at 1024 and
-// slower at 512; when its workgroups run in several rounds (Nq = 16384: 1024
-// workgroups) it is faster at some key counts and slower at others by up to
-// 17 %, varying from box to box with how its rounds share K and V in L2; so
-// it takes exactly the former.  ATTN_FA40=0 turns it off, ATTN_FA40=1 forces
-// it wherever d = 40 (for comparisons).
+// this file's.  Measured on MI355X (both kernels on one box, B=2, H=8,
+// per-launch medians, graph-replayed launches alike): the attn_fa40.hip kernel
+// is faster from 1536 keys on, by 3-11 % at Nq = 4096 (1536-16384 keys) and
+// 2-11 % at Nq = 16384 (1536-16384 keys, Q, K ~ N(0, 1.5^2)), level at 1024
+// keys and slower at 512; so it takes every problem with more than 1024 keys.
+// ATTN_FA40=0 turns it off, ATTN_FA40=1 forces it wherever d = 40 (for
+// comparisons).
 bool use_fa40(const Problem& p, int cus) {
   const char* e = std::getenv("ATTN_FA40");  // (read per launch: tests switch it)
   if (e && (e[0] == '0' || e[0] == '1')) return e[0] == '1';
-  return (long long)p.BH * ((p.Nq + 255) / 256) <= cus && p.Nk > 1024;
+  (void)cus;
+  return p.Nk > 1024;
 }
 
 // Whether a single pass takes the short-key-range kernel of attn_short.hip:

@@ -45,8 +45,7 @@ def kernel_source(kernel: str, cfg, cus: int = 256) -> str:
     attn_short.hip where Nk <= 384 (d = 40) or 256 (d = 80, 160) (ATTN_SHORT=0
     / 1 turn that off / force it within those limits); otherwise the single
     pass and the second pass at d = 40 take the kernels of attn_fa40.hip when
-    every 256-query workgroup is resident at once (B*H*ceil(Nq/256) <= the CU
-    count) and Nk > 1024 (ATTN_FA40=0 / 1 turn that off / force it); the
+    Nk > 1024 (ATTN_FA40=0 / 1 turn that off / force it); the
     general kernels of attn_mfma.hip take the rest."""
     half = cfg.dtype in ("f16", "bf16")
     short_max = {40: 384, 80: 256, 160: 256}.get(cfg.d, 0)
@@ -54,7 +53,7 @@ def kernel_source(kernel: str, cfg, cus: int = 256) -> str:
     if half and kernel == "attn_flash" and cfg.Nk <= short_max and env_s != "0":
         return os.path.join(CSRC, "attn_short.hip")
     env = os.environ.get("ATTN_FA40", "")[:1]
-    rule = cfg.B * cfg.H * -(-cfg.Nq // 256) <= cus and cfg.Nk > 1024
+    rule = cfg.Nk > 1024
     on = {"0": False, "1": True}.get(env, rule)
     fa40 = cfg.d == 40 and half and kernel in ("attn_flash", "attn_pv") and on
     return os.path.join(CSRC, "attn_fa40.hip" if fa40 else "attn_mfma.hip")

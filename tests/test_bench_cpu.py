@@ -83,7 +83,7 @@ def test_kernel_source_follows_the_dispatch(monkeypatch):
     assert bench.kernel_source("attn_pv", c1).endswith("attn_fa40.hip")
     assert bench.kernel_source("attn_stats", c1).endswith("attn_mfma.hip")
     assert bench.kernel_source("attn_flash", CONFIGS["level2_self"]).endswith("attn_mfma.hip")  # 1024 keys
-    assert bench.kernel_source("attn_flash", CONFIGS["sd1024_self"]).endswith("attn_mfma.hip")  # 1024 workgroups
+    assert bench.kernel_source("attn_flash", CONFIGS["sd1024_self"]).endswith("attn_fa40.hip")  # 16384 keys
     for name in ("sd512_cross", "level3_self", "level4_self"):  # 77, 256, 64 keys
         assert bench.kernel_source("attn_flash", CONFIGS[name]).endswith("attn_short.hip")
         assert bench.kernel_source("attn_pv", CONFIGS[name]).endswith("attn_mfma.hip")
