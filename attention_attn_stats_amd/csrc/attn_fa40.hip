@@ -27,8 +27,9 @@
 //    four-slot ring per key split, issued two blocks ahead and waited for just
 //    before the one barrier per block; no registers hold staged data.
 //  * The single pass keeps one reference max per query: the exact max of the
-//    first tile.  Scores beyond it by up to 16 (exp2 units) keep P finite in
-//    fp16; a row whose sum comes out non-finite or above 2^50 is recomputed by
+//    first tile (in fp16, 4 exp2 units above it).  Scores beyond the reference
+//    by up to 16 keep P finite in fp16; a row whose sum comes out non-finite
+//    or above 2^50 is recomputed by
 //    the whole workgroup with a reference that follows the running max tile
 //    by tile (exact online softmax), so the fast path needs no per-tile test.
 //  * Keys past Nk: their K rows and V rows read as zero (buffer range check)
