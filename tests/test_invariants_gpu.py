@@ -135,6 +135,29 @@ def test_rising_scores_rebase_every_block(form, dtype, d):
     assert_close_ml(from_device(ml), ml_ref, f"{form}/{dtype}/d{d} rising scores")
 
 
+@pytest.mark.parametrize("gap", [15.5, 17.8, 19.5])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_late_key_within_the_fast_path_headroom(gap, dtype):
+    # every query scores ~0 on every key but one late key, which scores `gap`
+    # (exp2 units) above the first tile: beyond 16 the fp16 single pass keeps
+    # P finite only through the 4 units of headroom of its reference max, with
+    # P of that key up to 2^15.5 (no recompute of the pass)
+    B, H, Nq, Nk, d = 1, 1, 64, 2048, 40
+    scale = float(np.float32(1 / np.sqrt(d)))
+    q = np.zeros((B, H, Nq, d))
+    q[..., 0] = 1.0
+    q[..., 1:] = synth.normal(71, Nq * (d - 1)).reshape(B, H, Nq, d - 1) * 0.05
+    k = synth.normal(72, Nk * d).reshape(B, H, Nk, d) * 0.05
+    k[0, 0, 1500, :] = 0.0
+    k[0, 0, 1500, 0] = gap / (scale * np.log2(np.e))
+    q, k = synth.round_to(q, dtype), synth.round_to(k, dtype)
+    v = synth.tensor(73, (B, H, Nk, d), dtype)
+    o, ml = _forward(*(to_device(x, dtype) for x in (q, k, v)), "flash", scale)
+    o_ref, ml_ref = reference(q, k, v, dtype, scale)
+    assert_close_o(from_device(o), o_ref, dtype, f"late key {gap} above the first tile")
+    assert_close_ml(from_device(ml), ml_ref, f"late key {gap} above the first tile")
+
+
 @pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_peaked_softmax_large_logits(form, dtype):
