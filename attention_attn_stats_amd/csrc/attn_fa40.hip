@@ -161,6 +161,26 @@ __device__ __forceinline__ float row_sum(float a, float b, int l32) {
   return l32 < 16 ? la : lb;
 }
 
+// Q^T operand of the score product for query `row` (rows past Nq read as
+// zero): lane half hi holds dims 16 ks + 8 hi .. + 7; dims 40-47 hold the
+// mask weight -2^15 (dim 40) and zeros
+template <class TR>
+__device__ __forceinline__ void load_q_operand(s8v (&qf)[3], const uint16_t* qh, int qrow_stride, int row, int hi,
+                                               int Nq) {
+  const bool ok = row < Nq;
+  const uint16_t* qp = qh + (size_t)(ok ? row : 0) * qrow_stride;
+#pragma unroll
+  for (int ks = 0; ks < 3; ++ks) {
+    const int d0 = ks * 16 + hi * 8;
+    if (d0 < D) {
+      const uint4 x = *(const uint4*)(qp + d0);
+      qf[ks] = ok ? __builtin_bit_cast(s8v, x) : (s8v){0, 0, 0, 0, 0, 0, 0, 0};
+    } else {
+      qf[ks] = (s8v){(short)TR::kMinus2p15, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+}
+
 }  // namespace fa40
 
 // ---------------------------------------------------------------------------
@@ -182,6 +202,10 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
   constexpr bool kML = MODE == kModeFlashML;
   // bf16-rounded P is too coarse for a reported l: sum the fp32 P as well
   constexpr bool kValuSum = kML && !TR::kRoundedSumOk;
+  // fp16 O-only fast path: the scale and the reference max go into the score
+  // product (Q scaled into exp2 units in fp16, -reference against a K dim of
+  // 1.0), so that P is exp2 of the product's result with no vector FMA
+  constexpr bool kFold = MODE == kModeFlash && TR::kPackedMax;
   __shared__ __attribute__((aligned(16))) uint8_t smem_[C::SMEM];
   __shared__ int redo_flag;
   // the LDS address of the array (a generic pointer into LDS keeps it in its low 32 bits)
@@ -212,23 +236,26 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
 
   // ---- Q^T operand (B of the score product): query l32, dims 16 ks + 8 hi;
   // dims 40-47 hold the mask weight -2^15 (dim 40) and zeros.  The scale
-  // stays out of the 16-bit operand.
+  // stays out of the 16-bit operand (but see fold_q).
   s8v qf[3];
-  {
-    const int row = qbase + l32;
-    const bool ok = row < Nq;
-    const uint16_t* qp = qh + (size_t)(ok ? row : 0) * lay.q.row;
+  load_q_operand<TR>(qf, qh, lay.q.row, qbase + l32, hi, Nq);
+  // the fp16 fast path after the first tile: Q scaled by c and rounded to
+  // fp16, dim 41 = -mr (mr itself an fp16 value, so the reference is exact)
+  auto fold_q = [&](float mr) __attribute__((always_inline)) {
+    typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 #pragma unroll
     for (int ks = 0; ks < 3; ++ks) {
-      const int d0 = ks * 16 + hi * 8;
-      if (d0 < D) {
-        const uint4 x = *(const uint4*)(qp + d0);
-        qf[ks] = ok ? __builtin_bit_cast(s8v, x) : (s8v){0, 0, 0, 0, 0, 0, 0, 0};
-      } else {
-        qf[ks] = (s8v){(short)TR::kMinus2p15, 0, 0, 0, 0, 0, 0, 0};
+      h8v x = __builtin_bit_cast(h8v, qf[ks]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = (_Float16)((float)x[e] * c);
+      if (ks == 2) {
+        h8v m = __builtin_bit_cast(h8v, (s8v){(short)TR::kMinus2p15, 0, 0, 0, 0, 0, 0, 0});
+        m[1] = (_Float16)(-mr);
+        x = hi ? m : x;  // lanes hi = 1 hold dims 40-47
       }
+      qf[ks] = __builtin_bit_cast(s8v, x);
     }
-  }
+  };
 
   // ---- direct-load plan of this wave: jobs qg, qg + QG, ... of the 13 per
   // block (7 K loads, then 6 V loads), each 64 chunks of 16 bytes
@@ -348,11 +375,16 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
     mma16_acc<TR>(wop, __builtin_bit_cast(s8v, (uint4){r0[1], r1[1], r2[1], r3[1]}), ob);
   };
   float mref = 0.f, mtrue = -INFINITY, lsum = 0.f;
+  // the folded fast path holds for references within +-64: beyond, the fp16
+  // reference loses range and Q's rounding weighs more, so the workgroup redoes
+  // its rows on the exact pass, which keeps the scale in fp32
+  bool fold_bad = false;
   // P of a score tile against mref, rounded and packed (the fast path)
-  auto expo = [&](const f16v& s, uint32_t (&pp)[8]) __attribute__((always_inline)) {
+  // (folded: the scores are already c s - mref)
+  auto expo = [&](const f16v& s, uint32_t (&pp)[8], bool folded) __attribute__((always_inline)) {
     float p[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -mref));
+    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(folded ? s[i] : __builtin_fmaf(s[i], c, -mref));
 #pragma unroll
     for (int i = 0; i < 8; ++i) pp[i] = TR::pack2(p[2 * i], p[2 * i + 1]);
     if constexpr (kValuSum) {
@@ -375,7 +407,7 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
 
     lsum *= alpha;
     mref = mn;
-    expo(s, pp);
+    expo(s, pp, false);
   };
 
   if (tid == 0) redo_flag = 0;
@@ -384,6 +416,9 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
   // (a plain lambda inlined at its two call sites with a constant argument,
   // so that every test of `exact` folds away)
   auto run = [&](bool exact) __attribute__((always_inline)) {
+    if constexpr (kFold) {
+      if (exact) load_q_operand<TR>(qf, qh, lay.q.row, qbase + l32, hi, Nq);  // unscaled again
+    }
     o0 = (f16v){};
     oa = (f4v){};
     ob = (f4v){};
@@ -395,7 +430,7 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
       lds8* sl = ring + (e / BN) * SLOT;
       const int key = e % BN;
       lds_store16(sl + KBYTES + 16 * (VGRP * (key >> 2) + 20 + (key & 3)), TR::kOne, 0, 0, 0);
-      lds_store16(sl + key * KPITCH + 80, 0, 0, 0, 0);
+      lds_store16(sl + key * KPITCH + 80, kFold ? (uint32_t)TR::kOne << 16 : 0u, 0, 0, 0);
     }
     wait_lds();
     barrier();  // the chunks are written before any direct load of the pass lands next to them
@@ -423,9 +458,16 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
         // that scores up to 16 + kHeadroom above it stay finite
         mref = (!exact && TR::kPackedMax) ? m0 + kHeadroom : m0;
         if (exact || kML) mtrue = m0;
+        if constexpr (kFold) {
+          if (!exact) {
+            mref = (float)(_Float16)mref;
+            fold_bad = !(__builtin_fabsf(mref) <= 64.f);
+            fold_q(mref);
+          }
+        }
       }
       s1 = qk(ring, 1);
-      expo(s0, pa);
+      expo(s0, pa, false);
     }
     // one tile step: P of `cur` into `pout`, scores of the next tile into
     // `snext` (when there is one), PV of the previous tile (`pin`)
@@ -437,7 +479,7 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
         expo_exact(cur, pout);
       } else {
         if constexpr (kML) mtrue = __builtin_fmaxf(mtrue, tile_max(cur) * c);
-        expo(cur, pout);
+        expo(cur, pout, kFold);
       }
     };
     // full bodies: tiles 2b+1 and 2b+2, scores of block b+1, PV of block b
@@ -481,7 +523,7 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
   float lrow = row_sum(mfma_settled(oa[0]), mfma_settled(ob[0]), l32);
   if constexpr (!kPV) {
     // a row whose sum left the fast path's range is recomputed by all waves
-    if (nb > 0 && __any(!(lrow < kSumLimit))) redo_flag = 1;
+    if (nb > 0 && __any(!(lrow < kSumLimit) || fold_bad)) redo_flag = 1;
     wait_lds();
     barrier();
     if (redo_flag) {
