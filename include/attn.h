@@ -110,7 +110,12 @@ attn_status attn_pv(const void* q, const void* k, const void* v, const float* ml
 /* FlashAttention forward: one launch, tiled over keys with the online
  * (running max / running sum) softmax, exact up to rounding (write-up,
  * attention section).  ml_out may be NULL; if given, the final (m, l) of every
- * row is written in the same convention as attn_stats. */
+ * row is written in the same convention as attn_stats.  With dt = ATTN_F16,
+ * d = 40, more than 1024 keys (any key count when the environment sets
+ * ATTN_FA40=1; none with ATTN_FA40=0) and ml_out NULL, the scores are formed from q
+ * scaled by scale * log2(e) and rounded to fp16 (a relative 2^-11 per product
+ * term on top of the float32 accumulation); rows whose first 32 keys put the
+ * reference beyond +-64 (exp2 units) are recomputed with the scale in float32. */
 attn_status attn_flash(const void* q, const void* k, const void* v, void* out, float* ml_out,
                        int B, int H, int Nq, int Nk, int d, float scale, attn_dtype dt,
                        void* stream);
