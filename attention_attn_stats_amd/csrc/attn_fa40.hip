@@ -246,14 +246,22 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
   s8v qf[3];
   load_q_operand<TR>(qf, qh, lay.q.row, qbase + l32, hi, Nq);
   // the fp16 fast path after the first tile: Q scaled by c and rounded to
-  // fp16, dim 41 = -mr (mr itself an fp16 value, so the reference is exact)
+  // fp16, dim 41 = -mr (mr itself an fp16 value, so the reference is exact);
+  // true if a scaled element of the query leaves fp16's finite range
   auto fold_q = [&](float mr) __attribute__((always_inline)) {
     typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+    float big = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 3; ++ks) {
       h8v x = __builtin_bit_cast(h8v, qf[ks]);
+      float bk = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = (_Float16)((float)x[e] * c);
+      for (int e = 0; e < 8; ++e) {
+        const float y = (float)x[e] * c;
+        bk = __builtin_fmaxf(bk, __builtin_fabsf(y));
+        x[e] = (_Float16)y;
+      }
+      big = (ks < 2 || !hi) ? __builtin_fmaxf(big, bk) : big;  // dims 0-39 only
       if (ks == 2) {
         h8v m = __builtin_bit_cast(h8v, (s8v){(short)TR::kMinus2p15, 0, 0, 0, 0, 0, 0, 0});
         m[1] = (_Float16)(-mr);
@@ -261,6 +269,7 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
       }
       qf[ks] = __builtin_bit_cast(s8v, x);
     }
+    return !(big < 65504.f);
   };
 
   // ---- direct-load plan of this wave: jobs qg, qg + QG, ... of the 13 per
@@ -381,9 +390,11 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
     mma16_acc<TR>(wop, __builtin_bit_cast(s8v, (uint4){r0[1], r1[1], r2[1], r3[1]}), ob);
   };
   float mref = 0.f, mtrue = -INFINITY, lsum = 0.f;
-  // the folded fast path holds for references within +-64: beyond, the fp16
-  // reference loses range and Q's rounding weighs more, so the workgroup redoes
-  // its rows on the exact pass, which keeps the scale in fp32
+  // the folded fast path holds for references within +-64 and a scaled query
+  // within fp16's range: beyond, the fp16 reference loses range and Q's
+  // rounding weighs more, or a score comes out infinite (a key's true score
+  // can then still weigh), so the workgroup redoes its rows on the exact
+  // pass, which keeps the scale in fp32
   bool fold_bad = false;
   // P of a score tile against mref, rounded and packed (the fast path)
   // (folded: the scores are already c s - mref)
@@ -467,8 +478,8 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
         if constexpr (kFold) {
           if (!exact) {
             mref = (float)(_Float16)mref;
-            fold_bad = !(__builtin_fabsf(mref) <= 64.f);
-            fold_q(mref);
+            const bool overflow = fold_q(mref);
+            fold_bad = overflow || !(__builtin_fabsf(mref) <= 64.f);
           }
         }
       }

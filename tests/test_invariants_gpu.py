@@ -194,6 +194,28 @@ def test_large_first_tile_reference_redoes_exactly(dtype, form):
         assert_close_ml(from_device(ml), ml_ref, f"{form}: large first-tile reference")
 
 
+def test_scaled_query_overflow_redoes_exactly():
+    # scale 2 and a query element of 60000: scaled into exp2 units (x 2.885)
+    # it leaves fp16's range.  Keys 0-127 (the first tiles of both key
+    # splits) have dim 0 = 0, so the reference stays near 0; keys from 128 on
+    # have dim 0 = -2e-5 (an fp16 subnormal), true scores near -2.4, about
+    # half of each row's weight, which an infinite scaled element would turn
+    # into -inf scores and drop without any non-finite sum.  The overflow
+    # itself sends the workgroup to the exact pass.  Half the queries carry
+    # the large element.
+    B, H, Nq, Nk, d, dtype, scale = 1, 1, 256, 1500, 40, "f16", 2.0
+    q = synth.normal(91, B * H * Nq * d).reshape(B, H, Nq, d) * 0.1
+    q[:, :, ::2, 0] = 60000.0
+    k = synth.normal(92, B * H * Nk * d).reshape(B, H, Nk, d) * 0.1
+    k[..., 0] = 0.0
+    k[:, :, 128:, 0] = -2e-5
+    q, k = synth.round_to(q, dtype), synth.round_to(k, dtype)
+    v = synth.tensor(93, (B, H, Nk, d), dtype)
+    o, _ = _forward(*(to_device(x, dtype) for x in (q, k, v)), "flash_o", scale)
+    o_ref, _ = reference(q, k, v, dtype, scale)
+    assert_close_o(from_device(o), o_ref, dtype, "scaled query beyond fp16")
+
+
 @pytest.mark.parametrize("form", FORMS_O)
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_peaked_softmax_large_logits(form, dtype):
