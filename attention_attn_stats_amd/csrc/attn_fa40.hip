@@ -21,9 +21,9 @@
 //    of the same rounded P the numerator used.
 //  * Each wave runs a software pipeline over 32-key tiles: while the vector
 //    ALU forms P of tile t (one FMA, one exp2, half a pack per score; no FMA
-//    in the fp16 O-only form), the
-//    matrix cores compute the scores of tile t+1 and accumulate P of tile t-1
-//    into O, so one wave alone keeps both units fed.
+//    in the fp16 O-only form), the matrix cores compute the scores of tile
+//    t+1 and accumulate P of tile t-1 into O, so one wave alone keeps both
+//    units fed.
 //  * K and V blocks (64 keys) reach LDS by direct buffer-to-LDS loads into a
 //    four-slot ring per key split, issued two blocks ahead and waited for just
 //    before the one barrier per block; no registers hold staged data.
@@ -37,7 +37,8 @@
 //    rounded to fp16, and dim 41 of Q holds -reference against a K dim 41 of
 //    1.0, so the score product itself yields the exp2 argument.  The scaled
 //    Q's rounding (2^-11 of each product term) is the form's one extra error;
-//    a reference beyond +-64 sends the workgroup to the exact pass.
+//    a reference beyond +-64, or a scaled element beyond fp16's range, sends
+//    the workgroup to the exact pass.
 //  * Keys past Nk: their K rows and V rows read as zero (buffer range check)
 //    and a mask column (K dim 40 = 1 for them, 0 otherwise, against a query
 //    dim 40 of -2^15) drives their scores to -2^15 * scale, so exp2 gives 0.
@@ -57,8 +58,9 @@ constexpr int BN = 64;         // keys per block (two 32-key tiles)
 constexpr int NBUF = 4;        // ring slots per key split
 constexpr int KH = 2;          // key splits per query group
 // K block: 64 rows of 112 bytes (7 chunks of 16 B: dims 0-39, the mask
-// chunk (dim 40 the mask, dim 41 the 1.0 of the folded reference), one unused); the 28-word pitch reads 16 consecutive rows by
-// ds_read_b128 without bank conflicts.
+// chunk (dim 40 the mask, dim 41 the 1.0 of the folded reference), one
+// unused); the 28-word pitch reads 16 consecutive rows by ds_read_b128
+// without bank conflicts.
 constexpr int KPITCH = 112;
 constexpr int KCH = 7;
 constexpr int KBYTES = BN * KPITCH;               // 7168
