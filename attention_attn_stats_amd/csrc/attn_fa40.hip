@@ -453,10 +453,11 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
     }
     wait_lds();
     barrier();  // the chunks are written before any direct load of the pass lands next to them
-    // blocks 0 and 1 land before the pass starts; blocks 2 and 3 are issued
-    // only then (with every workgroup of the chip starting at once, the
-    // first blocks would otherwise queue behind twice the bytes)
-    const int npre = nb < NBUF ? nb : NBUF, nfirst = npre < 2 ? npre : 2;
+    // block 0 lands before the pass starts; blocks 1-3 are issued only then
+    // (with every workgroup of the chip starting at once, the first block
+    // would otherwise queue behind the others' bytes), and block 1 is waited
+    // for after the first block's two score tiles
+    const int npre = nb < NBUF ? nb : NBUF, nfirst = npre < 1 ? npre : 1;
     for (int b = 0; b < nfirst; ++b) issue(b);
     wait_vm<0>();
     wait_lds();
@@ -488,6 +489,15 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
       s1 = qk(ring, 1);
       expo(s0, pa, false);
     }
+    // block 1 lands before the first body reads it (blocks 2, 3 may be in flight)
+    if (npre >= 4)
+      wait_vm<2 * C::MAXJ>();
+    else if (npre == 3)
+      wait_vm<C::MAXJ>();
+    else
+      wait_vm<0>();
+    wait_lds();
+    barrier();
     // one tile step: P of `cur` into `pout`, scores of the next tile into
     // `snext` (when there is one), PV of the previous tile (`pin`)
     auto step = [&](const lds8* ks, int kt, const lds8* vs, int vt, const f16v& cur, f16v& snext,
