@@ -292,8 +292,16 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
       dma.voff[r] = ((4 * grp + (rem & 3)) * vrs + ch * 8) * 2;
     }
   }
-  // issue the direct loads of local block b into its slot
-  auto issue = [&](int b) __attribute__((always_inline)) {
+  // the last block, if partial: K mask chunk 1.0 for its keys past Nk
+  auto mask_partial = [&](int b) __attribute__((always_inline)) {
+    if (has_partial && KH * b + splitu == kb_last && qgu == QG - 1) {
+      const int key = (KH * b + splitu) * BN + lane;
+      if (key >= Nk)
+        lds_store16(ring + (b % NBUF) * SLOT + lane * KPITCH + 80, TR::kOne, 0, 0, 0);
+    }
+  };
+  // issue the direct loads of local block b into its slot (and its mask chunks)
+  auto issue = [&](int b, bool with_mask) __attribute__((always_inline)) {
     const int key0 = (KH * b + splitu) * BN;
     const unsigned kbytes = Nk > key0 ? ((unsigned)(Nk - key0 - 1) * (unsigned)krs + D) * 2u : 0u;
     const unsigned vbytes = Nk > key0 ? ((unsigned)(Nk - key0 - 1) * (unsigned)vrs + D) * 2u : 0u;
@@ -311,12 +319,7 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
         dma16(kr, smem + DUMMY, dma.voff[r]);
       }
     }
-    // the last block, if partial: K mask chunk 1.0 for its keys past Nk
-    if (has_partial && KH * b + splitu == kb_last && qgu == QG - 1) {
-      const int key = key0 + lane;
-      if (key >= Nk)
-        lds_store16(sl + lane * KPITCH + 80, TR::kOne, 0, 0, 0);
-    }
+    if (with_mask) mask_partial(b);
   };
 
   // ---- per-lane LDS offsets within a slot
@@ -444,6 +447,10 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
     oscale = 1.f;
     lsum = 0.f;
     mtrue = -INFINITY;
+    const int npre = nb < NBUF ? nb : NBUF, nfirst = npre < 1 ? npre : 1;
+    // block 0's direct loads go out first: they write none of the constant
+    // chunks below (its mask chunks, if it is the partial block, follow them)
+    if (nfirst > 0) issue(0, false);
     // V ones chunks and K mask chunks of every slot of this split
     for (int e = tid % C::HT; e < NBUF * BN; e += C::HT) {
       lds8* sl = ring + (e / BN) * SLOT;
@@ -452,17 +459,16 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
       lds_store16(sl + key * KPITCH + 80, kFold ? (uint32_t)TR::kOne << 16 : 0u, 0, 0, 0);
     }
     wait_lds();
-    barrier();  // the chunks are written before any direct load of the pass lands next to them
+    barrier();  // every constant chunk is written before a partial block's mask chunks
     // block 0 lands before the pass starts; blocks 1-3 are issued only then
     // (with every workgroup of the chip starting at once, the first block
     // would otherwise queue behind the others' bytes), and block 1 is waited
     // for after the first block's two score tiles
-    const int npre = nb < NBUF ? nb : NBUF, nfirst = npre < 1 ? npre : 1;
-    for (int b = 0; b < nfirst; ++b) issue(b);
+    if (nfirst > 0) mask_partial(0);
     wait_vm<0>();
     wait_lds();
     barrier();
-    for (int b = nfirst; b < npre; ++b) issue(b);
+    for (int b = nfirst; b < npre; ++b) issue(b, true);
 
     uint32_t pa[8], pb[8];
     f16v s1 = (f16v){};
@@ -526,7 +532,7 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
       wait_vm<C::MAXJ>();
       wait_lds();
       barrier();
-      if (b + NBUF < nb) issue(b + NBUF);
+      if (b + NBUF < nb) issue(b + NBUF, true);
     }
     for (; b < nb - 1; ++b) {
       body(b);
