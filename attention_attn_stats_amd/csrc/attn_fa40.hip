@@ -310,14 +310,11 @@ __global__ __launch_bounds__((fa40::Cfg<QG>::T)) void fa40_kernel(const uint16_t
     lds8* const sl = ring + (b % NBUF) * SLOT;
 #pragma unroll
     for (int r = 0; r < C::MAXJ; ++r) {
+      // the job's source and slot chunk chosen by wave-uniform selects, not branches
       const int j = qgu + QG * r;
-      if (j < KJOBS) {
-        if (dma.act[r]) dma16(kr, sl + 1024 * j, dma.voff[r]);
-      } else if (j < NJOBS) {
-        if (dma.act[r]) dma16(vr, sl + KBYTES + 1024 * (j - KJOBS), dma.voff[r]);
-      } else {
-        dma16(kr, smem + DUMMY, dma.voff[r]);
-      }
+      const bool isv = j >= KJOBS && j < NJOBS;
+      lds8* const dst = j < NJOBS ? sl + (j < KJOBS ? 1024 * j : KBYTES + 1024 * (j - KJOBS)) : smem + DUMMY;
+      if (dma.act[r]) dma16(isv ? vr : kr, dst, dma.voff[r]);
     }
     if (with_mask) mask_partial(b);
   };
